@@ -1,0 +1,113 @@
+"""Seeded synthetic inputs for attention workloads.
+
+This module holds no attention arithmetic.  It draws Q, K, V and key lengths
+from a seeded generator and rounds them to the storage dtype; the GPU path
+and the CPU oracle both receive exactly these bits.
+
+Recipe (one generator per workload):
+  * ``numpy.random.Generator(PCG64(seed)).standard_normal(shape)`` in float64,
+    drawn in the order Q, K, V, each whole tensor in C order;
+  * multiplied by ``value_scale`` (a power of two, so exact), cast to float32,
+    then rounded to bfloat16 with round-to-nearest-even for bf16 workloads;
+  * then ``key_lens = integers(lo, hi + 1, size=B)`` (inclusive bounds) when
+    the workload has key padding.
+
+The shapes follow the pages' workloads: the base model's 8 heads of width 64
+and the big model's 16 heads ("序列建模架构的演进与变革（二）" §4.9 and the
+hugogu wiki "Transformer" page, which give d_model = 512, h = 8,
+d_k = d_v = 64), sentences padded to the batch maximum with lengths up to
+512 ("Transformer: 详解" §3.3), and a long causal stress shape.  Values are
+iid N(0, 1), for which the variance of q.k is d_k
+("序列建模架构的演进与变革（二）" §4.4).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    n: int
+    m: int
+    d: int
+    dtype: str                 # "f32" or "bf16"
+    causal: bool
+    lens: Optional[Tuple[int, int]]   # inclusive (lo, hi) for key_lens, or None
+    seed: int
+    value_scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    def metric_flops(self) -> float:
+        """4 * B * H * n * m * d, halved for causal attention."""
+        f = 4.0 * self.B * self.H * self.n * self.m * self.d
+        return f / 2.0 if self.causal else f
+
+
+WORKLOADS = {
+    "fp32_small": Workload(
+        "fp32_small", B=1, H=8, n=16, m=16, d=64, dtype="f32", causal=False,
+        lens=None, seed=0,
+        note="fp32, one batch of 8 heads, 16x16, no mask"),
+    "encoder_pad_n128": Workload(
+        "encoder_pad_n128", B=32, H=8, n=128, m=128, d=64, dtype="bf16",
+        causal=False, lens=(16, 128), seed=1,
+        note="encoder self-attention, key padding, lengths U{16..128}"),
+    "decoder_causal_n512": Workload(
+        "decoder_causal_n512", B=16, H=8, n=512, m=512, d=64, dtype="bf16",
+        causal=True, lens=None, seed=2,
+        note="decoder causal self-attention, no padding"),
+    "cross_n256_m1024": Workload(
+        "cross_n256_m1024", B=8, H=16, n=256, m=1024, d=64, dtype="bf16",
+        causal=False, lens=(512, 1024), seed=3,
+        note="cross-attention, 256 queries vs 1024 keys, key padding U{512..1024}"),
+    "causal_n16384_d128": Workload(
+        "causal_n16384_d128", B=1, H=16, n=16384, m=16384, d=128, dtype="bf16",
+        causal=True, lens=None, seed=4, value_scale=0.5,
+        note="long causal self-attention, values N(0,1)*0.5"),
+}
+
+ORDER = ["fp32_small", "encoder_pad_n128", "decoder_causal_n512",
+         "cross_n256_m1024", "causal_n16384_d128"]
+
+
+def _round(x64: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x64.astype(np.float32)))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)   # round to nearest even
+    if dtype == "f32":
+        return t
+    raise ValueError("dtype must be 'f32' or 'bf16'")
+
+
+def draw(B, H, n, m, dk, dv, dtype, seed, lens=None, value_scale=1.0):
+    """Draw (q, k, v, key_lens) on the CPU.
+
+    q, k, v are torch CPU tensors of the storage dtype; key_lens is an int32
+    numpy array of shape (B,) or None.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _round(rng.standard_normal((B, H, n, dk)) * value_scale, dtype)
+    k = _round(rng.standard_normal((B, H, m, dk)) * value_scale, dtype)
+    v = _round(rng.standard_normal((B, H, m, dv)) * value_scale, dtype)
+    key_lens = None
+    if lens is not None:
+        lo, hi = lens
+        key_lens = rng.integers(lo, hi + 1, size=B).astype(np.int32)
+    return q, k, v, key_lens
+
+
+def make(w: Workload):
+    """Inputs of a named workload: (q, k, v, key_lens)."""
+    return draw(w.B, w.H, w.n, w.m, w.d, w.d, w.dtype, w.seed, w.lens,
+                w.value_scale)
