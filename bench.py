@@ -1,0 +1,298 @@
+"""Benchmark of the attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one mha_forward call over one batch of the workload (default:
+causal self-attention, B=1, H=16, n=m=16384, d=128, bf16), with inputs
+already resident in HBM.  W untimed steps, then exactly K timed steps
+bracketed by device synchronisation; HIP events on the launch stream give
+the per-launch kernel duration.  Prints ONE JSON line with the headline
+TFLOP/s (4*B*H*n*m*d, halved for causal), a roofline object for the
+kernel, the other workloads (GB/s and TFLOP/s each against its roofline,
+inputs rotated over >= 1 GiB so the 256 MB last-level cache cannot serve
+repeats), and the CPU oracle timed on a bounded sample of the headline
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix/vector, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(_ROOT, "transformer_head_scaled_fwd_amd", "csrc",
+                          "mha_fwd_kernel.hip")
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "hbm_traffic_causal_n16384_d128.md")
+HEADLINE = "causal_n16384_d128"
+SECONDARY = "encoder_pad_n128"
+
+
+def algorithmic_bytes(w, key_lens) -> int:
+    """Q read once, O written once, only the valid K and V rows read once,
+    the int32 lengths; the score matrix contributes nothing."""
+    es = 2 if w.dtype == "bf16" else 4
+    kv_rows = w.B * w.m if key_lens is None else int(np.clip(key_lens, 0, w.m).sum())
+    return es * (2 * w.B * w.H * w.n * w.d + w.H * kv_rows * 2 * w.d) + \
+        (4 * w.B if key_lens is not None else 0)
+
+
+def valid_pairs(w, key_lens) -> int:
+    total = 0
+    for b in range(w.B):
+        L = w.m if key_lens is None else max(0, min(int(key_lens[b]), w.m))
+        if w.causal:
+            total += int(np.minimum(np.arange(w.n, dtype=np.int64) + 1, L).sum())
+        else:
+            total += w.n * L
+    return total * w.H
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when it is absent or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE, encoding="utf-8").read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "cus": p.multi_processor_count}
+    arch = getattr(p, "gcnArchName", None)
+    if arch:
+        info["arch"] = arch
+    clk = getattr(p, "clock_rate", None)
+    if clk:
+        info["clock_mhz"] = clk / 1000.0
+        info["bf16_mfma_tflops_from_props"] = p.multi_processor_count * 4096 * clk * 1e3 / 1e12
+    return info
+
+
+def upload(torch, w, seed_offset=0):
+    from transformer_head_scaled_fwd_amd import inputs
+    q, k, v, kl = inputs.draw(w.B, w.H, w.n, w.m, w.d, w.d, w.dtype, w.seed + seed_offset,
+                              w.lens, w.value_scale)
+    dev = "cuda:0"
+    kld = None if kl is None else torch.as_tensor(kl).to(dev)
+    return (q.to(dev), k.to(dev), v.to(dev), kld, kl), (q, k, v, kl)
+
+
+def time_launches(torch, mha, sets, w, steps, warmup):
+    """Warmup, then `steps` launches cycling over `sets`; per-launch event
+    pairs and one pair around the whole region, all on the launch stream."""
+    stream = torch.cuda.current_stream()
+    outs = [torch.empty((w.B, w.H, w.n, w.d), dtype=s[0].dtype, device="cuda:0") for s in sets]
+
+    def launch(i):
+        q, k, v, kl, _ = sets[i % len(sets)]
+        mha.forward(q, k, v, key_lens=kl, causal=w.causal, scale=w.scale,
+                    out=outs[i % len(sets)], stream=stream.cuda_stream)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return t0.elapsed_time(t1), per
+
+
+def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+    from transformer_head_scaled_fwd_amd import inputs
+    w = inputs.WORKLOADS[name]
+    first, host = upload(torch, w)
+    set_bytes = sum(t.numel() * t.element_size() for t in first[:3]) * 4 // 3
+    nsets = max(1, min(64, -(-rotate_bytes // max(set_bytes, 1))))
+    sets = [first]
+    # Distinct input sets so repeats cannot be served from the last-level cache;
+    # the extra sets reuse the first set's key lengths so every launch does
+    # the same work.
+    for s in range(1, nsets):
+        q, k, v = (torch.roll(t, shifts=s, dims=0).contiguous() + 0 for t in first[:3])
+        sets.append((q, k, v, first[3], first[4]))
+    total_ms, per = time_launches(torch, mha, sets, w, steps, warmup)
+    kl = first[4]
+    flops = w.metric_flops()
+    useful = 4.0 * w.d * valid_pairs(w, kl)
+    abytes = algorithmic_bytes(w, kl)
+    avg = total_ms / steps
+    kern = statistics.mean(per)
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    return {
+        "workload": name, "dtype": w.dtype, "B": w.B, "H": w.H, "n": w.n, "m": w.m,
+        "d": w.d, "causal": w.causal, "key_lens": None if w.lens is None else list(w.lens),
+        "input_sets": len(sets), "launches": steps,
+        "ms_per_launch": avg, "kernel_ms_mean": kern, "kernel_ms_median": statistics.median(per),
+        "kernel_ms_min": min(per),
+        "tflops": flops / (kern * 1e-3) / 1e12,
+        "frac_mfma_peak": flops / (kern * 1e-3) / 1e12 / peak,
+        "useful_tflops": useful / (kern * 1e-3) / 1e12,
+        "gbps": abytes / (kern * 1e-3) / 1e9,
+        "frac_hbm": abytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes": abytes, "metric_flops": flops,
+    }, host, sets
+
+
+def cpu_baseline(w, host, budget_s):
+    """The oracle as it stands, on a bounded sample of query rows of the
+    headline workload, timed on this host's cores."""
+    import oracle
+    q, k, v, kl = host
+    Q, K, V = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+    rng = np.random.Generator(np.random.PCG64(2024))
+
+    def sample(r):
+        b = rng.integers(0, w.B, r)
+        t = rng.integers(0, w.H, r)
+        i = rng.integers(0, w.n, r)
+        return np.stack([b, t, i], 1).astype(np.int64)
+
+    def work(rows):
+        keys = rows[:, 2] + 1 if w.causal else np.full(len(rows), w.m)
+        if kl is not None:
+            keys = np.minimum(keys, np.asarray(kl)[rows[:, 0]])
+        return 4.0 * w.d * float(keys.sum())
+
+    probe = sample(64)
+    t = time.perf_counter()
+    oracle.attention_rows(Q, K, V, probe, key_lens=kl, causal=w.causal, scale=w.scale)
+    dt = max(time.perf_counter() - t, 1e-3)
+    rate = work(probe) / dt
+    target = max(64, int(len(probe) * budget_s / dt))
+    rows = sample(min(target, 200000))
+    t = time.perf_counter()
+    oracle.attention_rows(Q, K, V, rows, key_lens=kl, causal=w.causal, scale=w.scale)
+    dt = time.perf_counter() - t
+    f = work(rows)
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": dt, "probe_rate_tflops": rate / 1e12,
+            "sample": "%d query rows drawn uniformly (seeded) from the %d heads of %s; "
+                      "useful FLOPs 4*d*(valid keys) per row; fp64 on the host cores"
+                      % (len(rows), w.B * w.H, w.name)}
+
+
+def calibrate_copy(torch, nbytes):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "launches": 3}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the attention kernel runs on one "
+              "device and no multi-GPU path is built (asked for --gpus %d, "
+              "WORLD_SIZE=%d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_head_scaled_fwd_amd as mha
+    from transformer_head_scaled_fwd_amd import inputs
+    mha.load()
+    if args.calibrate_copy:
+        calibrate_copy(torch, args.calibrate_copy)
+        return
+
+    w = inputs.WORKLOADS[args.workload]
+    print("bench: %s steps=%d warmup=%d" % (w.name, args.steps, args.warmup),
+          file=sys.stderr, flush=True)
+    head, host, _ = bench_workload(torch, mha, w.name, args.steps, args.warmup)
+    others = []
+    if not args.no_others:
+        for name in inputs.ORDER:
+            if name == w.name:
+                continue
+            print("bench: %s" % name, file=sys.stderr, flush=True)
+            res, _, sets = bench_workload(torch, mha, name, 200, 20)
+            del sets
+            others.append(res)
+            torch.cuda.empty_cache()
+    traffic = recorded_traffic() if w.name == HEADLINE else None
+    cpu = None
+    if not args.no_cpu:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, host, args.cpu_seconds)
+    bf16 = w.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_MFMA_TFLOPS
+    kern_s = head["kernel_ms_mean"] * 1e-3
+    achieved = head["metric_flops"] / kern_s / 1e12
+    sec = next((o for o in others if o["workload"] == SECONDARY), None)
+    line = {
+        "metric": "attention fwd TFLOP/s and % bf16 MFMA peak (causal n=16384, d=128); "
+                  "GB/s at n=128",
+        "value": head["metric_flops"] / (head["ms_per_launch"] * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["ms_per_launch"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "n": w.n, "m": w.m, "d": w.d,
+                   "causal": w.causal, "key_lens": None if w.lens is None else list(w.lens),
+                   "values": "N(0,1)*%g, seed %d" % (w.value_scale, w.seed)},
+        "frac_mfma_peak": head["frac_mfma_peak"],
+        "gbps_n128": None if sec is None else sec["gbps"],
+        "frac_hbm_n128": None if sec is None else sec["frac_hbm"],
+        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                     "kernel": "attn_fwd_kernel<bf16,%d,%s>" % (w.d, "causal" if w.causal else "full"),
+                     "kernel_ms_mean": head["kernel_ms_mean"],
+                     "kernel_ms_median": head["kernel_ms_median"],
+                     "kernel_source_sha256_16": kernel_source_hash(),
+                     "flops_per_launch": head["metric_flops"]},
+        "cpu_baseline": cpu,
+        "workloads": [head] + others,
+        "device": device_info(torch),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""libmha: multi-head scaled dot-product attention forward on MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/libmha.h.  This module only
+marshals arguments (device pointers, sizes, the current HIP stream); every
+step of the attention runs in the HIP kernels of libmha.so.  torch supplies
+device memory and the stream.  There is no fallback: if libmha.so is not
+built, every call raises.
+
+    import transformer_head_scaled_fwd_amd as mha
+    o = mha.forward(q, k, v, key_lens=None, causal=False, scale=None)
+
+q [B,H,n,d], k [B,H,m,d], v [B,H,m,d] contiguous bf16 or fp32 tensors on
+one GPU; key_lens an int32 tensor [B] on the same GPU (or None); scale
+defaults to the fp32 value of 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmha.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "libmha.h")
+
+MHA_F32 = 0
+MHA_BF16 = 1
+
+_lib = None
+
+
+class MhaError(ValueError):
+    """A non-zero status from libmha; .status holds the code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load():
+    """Load libmha.so (once).  Raises RuntimeError if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libmha.so is not built (expected at %s); run "
+            "`python -m transformer_head_scaled_fwd_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mha_abi_version.argtypes = []
+    lib.mha_abi_version.restype = i32
+    lib.mha_status_string.argtypes = [i32]
+    lib.mha_status_string.restype = ctypes.c_char_p
+    lib.mha_validate.argtypes = [vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                 i64, i64, i64, i64, i64, i64, i32]
+    lib.mha_validate.restype = i32
+    lib.mha_forward.argtypes = [vp, vp, vp, vp, i32, ctypes.c_float, vp,
+                                i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_forward.restype = i32
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions include/libmha.h declares."""
+    with open(HEADER_PATH, encoding="utf-8") as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(mha_\w+)\s*\(", text, re.M)))
+
+
+def abi_version() -> int:
+    return int(load().mha_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load().mha_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MhaError(status, status_string(status))
+
+
+def default_scale(d: int) -> float:
+    """fp32 value of 1/sqrt(d), the scale of the pages' attention."""
+    import numpy as np
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MHA_BF16
+    if t.dtype == torch.float32:
+        return MHA_F32
+    raise TypeError("libmha takes bfloat16 or float32 tensors, got %s" % t.dtype)
+
+
+def validate(q, k, v, key_lens=None, causal=False, scale=None, out=None) -> int:
+    """Run the library's host-side argument check only; returns the status."""
+    B, H, n, dk = q.shape
+    m, dv = k.shape[2], v.shape[3]
+    sc = default_scale(dk) if scale is None else float(scale)
+    return int(load().mha_validate(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        None if key_lens is None else key_lens.data_ptr(), int(bool(causal)), sc,
+        None if out is None else out.data_ptr(), B, H, n, m, dk, dv, _dtype_code(q)))
+
+
+def forward(q, k, v, key_lens=None, causal=False, scale=None, out=None, stream=None):
+    """O = softmax(scale * Q K^T + mask) V per (batch, head), on the GPU.
+
+    Enqueued on `stream` (default: torch's current stream); returns `out`
+    (allocated if not given) without synchronizing.
+    """
+    import torch
+    lib = load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, L, d]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev or v.device != dev:
+        raise ValueError("q, k, v must be on the same GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    B, H, n, dk = q.shape
+    m = k.shape[2]
+    dv = v.shape[3]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != dk or \
+            v.shape[0] != B or v.shape[1] != H or v.shape[2] != m:
+        raise ValueError("shape mismatch: q %s, k %s, v %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != dev or \
+                tuple(key_lens.shape) != (B,) or not key_lens.is_contiguous():
+            raise ValueError("key_lens must be a contiguous int32 tensor [B] on the GPU of q")
+        kl_ptr = key_lens.data_ptr()
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H, n, dv) or out.dtype != q.dtype or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, n, d_v] tensor like q")
+    sc = default_scale(dk) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.mha_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), kl_ptr,
+                             int(bool(causal)), sc, out.data_ptr(),
+                             B, H, n, m, dk, dv, code, stream)
+    _check(st)
+    return out
+
+
+__all__ = ["forward", "validate", "load", "abi_version", "status_string",
+           "header_functions", "default_scale", "MhaError", "LIB_PATH",
+           "MHA_F32", "MHA_BF16"]

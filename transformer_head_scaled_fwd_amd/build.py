@@ -1,0 +1,58 @@
+"""Build libmha.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+    python -m transformer_head_scaled_fwd_amd.build
+
+hipcc cross-compiles for gfx950 without a GPU present.  The packed-fp32
+target feature is switched off for all device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libmha.so")
+
+SOURCES = ["mha_abi.hip", "mha_fwd_kernel.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def command(out: str = LIB):
+    return ([hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC]
+            + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out])
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libmha.so; returns its path."""
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = command(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass does not know the gfx target feature; that warning
+    # is expected, anything else is shown.
+    noise = "is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if msgs and verbose:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
