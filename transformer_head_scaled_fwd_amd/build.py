@@ -50,8 +50,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
+    check_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_stubs(path: str) -> None:
+    """Fail if a kernel's host launch stub is missing from the library.
+
+    clang drops the stub of a kernel whose body is invalid for the host
+    pass (for example a device-only builtin inside a lambda) without an
+    error; the library would then fail to load at run time."""
+    res = subprocess.run(["nm", "-u", path], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in res.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(path)
+        raise RuntimeError("kernel launch stubs missing from the build: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

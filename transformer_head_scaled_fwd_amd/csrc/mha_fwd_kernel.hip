@@ -4,8 +4,9 @@
 // wave64s, each owning 32 rows.  It walks the key axis in blocks of BC = 64
 // keys.  Per block:
 //
-//   stage    K block -> LDS (row-major) and V block -> LDS (transposed),
-//            from 16-byte buffer loads issued one block ahead;
+//   stage    K and V blocks -> LDS, row-major, by buffer->LDS direct loads
+//            (no register staging), double-buffered: block kb+1 streams in
+//            while block kb is computed, one barrier per block;
 //   scores   S^T = K Q^T on MFMA (32x32 tiles, fp32 accumulate), Q held in
 //            registers for the whole walk;
 //   mask     -inf where j >= L_b or (causal and j > i)
@@ -14,7 +15,9 @@
 //            and log2(e) folded into one FMA, rescale of the output only when
 //            the row max grew by more than 2^TAU ("Transformer" wiki page:
 //            mixed precision needs the blockwise, online softmax);
-//   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype.
+//   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype; the V
+//            operand comes straight from the row-major tile through the
+//            LDS transpose read (ds_read_b64_tr_b16).
 //
 // The n x m score matrix exists only as register tiles and never reaches
 // memory ("Transformer: 详解" §8.2: the n^2 score/weight matrices are what
@@ -27,6 +30,10 @@
 // in-lane reductions plus one exchange between lane halves, the P^T
 // accumulator feeds the PV MFMA as its B operand without leaving registers,
 // and the rescale factor of a row is a per-lane scalar.
+//
+// LDS tiles are stored in 16-byte chunks with the chunk index XOR-ed by a
+// function of the row ("swizzle"), chosen per read pattern so that the lanes
+// of one LDS read cycle hit distinct banks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,8 +47,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -63,76 +72,83 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
-// Value of the lane 32 positions away (lanes l and l^32 share a query row).
-__device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
-
-template <typename T>
-struct Elem;
-
-// bf16 operands: v_mfma_f32_32x32x16_bf16.  A (32x16): lane l supplies row
-// l%32, k = 8(l/32)..+7; B (16x32): column l%32, same k.
-template <>
-struct Elem<__bf16> {
-  static constexpr int kBytes = 2;
-  static constexpr int kK = 16;  // contraction depth of one MFMA
-};
-
-// fp32 operands: v_mfma_f32_32x32x2_f32.  A: lane l supplies row l%32,
-// k = l/32; B: column l%32, k = l/32.
-template <>
-struct Elem<float> {
-  static constexpr int kBytes = 4;
-  static constexpr int kK = 2;
-};
-
-// Position of key u (0..15 within a group of 16) in the transposed bf16 V
-// tile: bits 2 and 3 swapped, so that the 8 keys a lane feeds to one PV MFMA
-// are contiguous (see the P packing in the main loop).
-__device__ inline int vt_pos16(int j) {
-  return (j & ~15) | ((j & 4) << 1) | ((j & 8) >> 1) | (j & 3);
+// max / sum of x over lanes l and l^32 (the two lanes that share a query
+// row).  v_permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second; called with (x, x) each lane receives
+// both its own value and its partner's, in an order that depends on the
+// half, so only symmetric combinations are formed from the pair.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                  __builtin_bit_cast(uint32_t, x), false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
-template <typename T, int D, bool CAUSAL>
-struct Tile {
-  static constexpr int ES = Elem<T>::kBytes;
-  static constexpr int KROW = D * ES + 16;   // K tile row stride (bytes), padded
-  static constexpr int VROW = BC * ES + 16;  // transposed V tile row stride, padded
-  static constexpr int K_BYTES = BC * KROW;
-  static constexpr int V_BYTES = D * VROW;
-  static constexpr int LDS_BYTES = K_BYTES + V_BYTES;
-  static constexpr int CPR = D * ES / 16;            // 16-byte chunks per row
-  static constexpr int K_CHUNKS = BC * CPR / kThreads;  // per thread
-  // V staging: each thread owns VR consecutive rows x one 16-byte chunk.
-  static constexpr int V_ITEMS = BC * CPR;             // (row, chunk) pairs
-  static constexpr int VR = V_ITEMS / kThreads;        // rows per thread (>= 1)
-  static constexpr int VR_TOTAL = VR;                  // loads per thread
-  static_assert(BC * CPR % kThreads == 0, "K staging must tile the workgroup");
-  static_assert(VR == 2 || VR == 4 || VR == 8, "V staging needs 2, 4 or 8 rows per thread");
-};
-
-// Which (row group, chunk) a thread stages for the transposed V tile.
+// Tile geometry and LDS swizzles.  ES: element bytes; CPR: 16-byte chunks
+// per row of D elements.
 template <typename T, int D>
-__device__ inline void v_item(int tid, int& row0, int& chunk) {
-  constexpr int CPR = D * Elem<T>::kBytes / 16;
-  constexpr int VR = (BC * CPR) / kThreads;
-  chunk = tid % CPR;
-  row0 = (tid / CPR) * VR;
-}
+struct Geo {
+  static constexpr int ES = sizeof(T);
+  static constexpr bool BF16 = (ES == 2);
+  static constexpr int ROWB = D * ES;          // bytes per K or V row in LDS
+  static constexpr int CPR = ROWB / 16;        // chunks per row: 8, 16 or 32
+  static constexpr int TILE = BC * ROWB;       // one K or one V block
+  static constexpr int STAGE = 2 * TILE;       // K + V
+  static constexpr int LDS_BYTES = 2 * STAGE;  // double-buffered
+  // direct-load instructions per wave for one tile (each moves 1 KiB)
+  static constexpr int LOADS = TILE / 1024 / kWaves;
+  static_assert(TILE % (1024 * kWaves) == 0, "tile must split into 1 KiB loads per wave");
+
+  // K is read by rows j = 0..31 of one 16-byte column chunk per MFMA
+  // operand: make the chunk position differ across 16 consecutive rows.
+  __device__ static inline int swz_k(int r) { return CPR == 8 ? ((r >> 1) & 7) : (r & 15); }
+  // V, bf16: the transpose read touches rows 4h..4h+3 x 4 chunks per 32 lanes;
+  // fp32: 32 consecutive elements of rows j and j+4.
+  __device__ static inline int swz_v(int r) {
+    if constexpr (BF16) return CPR == 8 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+    else return 8 * ((r >> 2) & 1);
+  }
+
+  // Direct loads of key/value block kb into LDS stage st.  Load u of a wave
+  // fills LDS bytes [1 KiB * (u * kWaves + wave), +1 KiB) of each tile; lane
+  // t writes the 16 bytes at +16t, i.e. chunk position pc of row r, which
+  // holds global chunk pc ^ swizzle(r).  Rows at or beyond `bytes` read as 0.
+  __device__ static inline void stage(char* smem, const T* kbase, const T* vbase, uint32_t bytes,
+                                      int kb, int st, int wave, int lane) {
+    const auto rk = make_rsrc(kbase, bytes);
+    const auto rv = make_rsrc(vbase, bytes);
+    char* kt = smem + st * STAGE;
+    char* vt = kt + TILE;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int slot = (u * kWaves + wave) * 64;  // first chunk of this load
+      const int q = slot + lane;
+      const int r = q / CPR, pc = q % CPR;
+      const uint32_t row_off = ((uint32_t)(kb * BC + r) * D) * ES;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + slot * 16), 16,
+                                               row_off + (pc ^ swz_k(r)) * 16, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + slot * 16), 16,
+                                               row_off + (pc ^ swz_v(r)) * 16, 0, 0, 0);
+    }
+  }
+};
 
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 2)
 attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
                 const T* __restrict__ Vp, const int32_t* __restrict__ key_lens,
                 T* __restrict__ Op, int H, int n, int m, int nqb, float scale_log2) {
-  using TL = Tile<T, D, CAUSAL>;
-  constexpr int ES = TL::ES;
-  constexpr bool BF16 = (ES == 2);
-  __shared__ __attribute__((aligned(16))) char smem[TL::LDS_BYTES];
-  char* Ks = smem;
-  char* Vt = smem + TL::K_BYTES;
+  using G = Geo<T, D>;
+  constexpr int ES = G::ES;
+  constexpr bool BF16 = G::BF16;
+  __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64;
   const int li = lane % 32;  // query row within the wave's 32 (MFMA column)
   const int hi = lane / 32;  // which half of the k / row groups this lane holds
@@ -158,13 +174,13 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // Last key block any row of this wave can see.
   const int wave_nkb = CAUSAL ? min(nkb, (row_w + kRowsPerWave + BC - 1) / BC) : nkb;
 
-  // Buffer resources: out-of-range loads read 0 and out-of-range stores are
-  // dropped, so rows >= n (queries) and >= L (keys, values) need no branch.
+  // Buffer resources: out-of-range loads read 0 (also into LDS) and
+  // out-of-range stores are dropped, so rows >= n (queries) and >= L (keys,
+  // values) need no branch and padded keys are never read from memory.
   const size_t head_q = (size_t)bh * (size_t)n * D;
   const size_t head_k = (size_t)bh * (size_t)m * D;
   const auto rq = make_rsrc(Qp + head_q, (uint32_t)n * D * ES);
-  const auto rk = make_rsrc(Kp + head_k, (uint32_t)L * D * ES);
-  const auto rv = make_rsrc(Vp + head_k, (uint32_t)L * D * ES);
+  const uint32_t kv_bytes = (uint32_t)L * D * ES;  // rows >= L read as 0
   const auto ro = make_rsrc(Op + head_q, (uint32_t)n * D * ES);
 
   // ---- Q fragments (MFMA B operand of S^T = K Q^T), kept in registers ----
@@ -177,71 +193,10 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     uint32_t col = BF16 ? (16 * s + 8 * hi) : (4 * s + (D / 2) * hi);
     qf[s] = load16(rq, ((uint32_t)my_row * D + col) * ES);
   }
-
-  // ---- staging of one K/V block into registers, then into LDS ----
-  u32x4 kreg[TL::K_CHUNKS];
-  u32x4 vreg[TL::VR_TOTAL];
-  int v_row0, v_chunk;
-  v_item<T, D>(tid, v_row0, v_chunk);
-
-  auto fetch = [&](int kb) {
-    const uint32_t base = (uint32_t)kb * BC;
+  // Complete the Q loads here: otherwise the in-order memory counter makes
+  // every iteration of the key loop wait for its own prefetch as well.
 #pragma unroll
-    for (int u = 0; u < TL::K_CHUNKS; ++u) {
-      const int id = u * kThreads + tid;
-      const int r = id / TL::CPR, c = id % TL::CPR;
-      kreg[u] = load16(rk, ((base + r) * D) * ES + c * 16);
-    }
-#pragma unroll
-    for (int r = 0; r < TL::VR; ++r)
-      vreg[r] = load16(rv, ((base + v_row0 + r) * D) * ES + v_chunk * 16);
-  };
-
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < TL::K_CHUNKS; ++u) {
-      const int id = u * kThreads + tid;
-      const int r = id / TL::CPR, c = id % TL::CPR;
-      *reinterpret_cast<u32x4*>(Ks + r * TL::KROW + c * 16) = kreg[u];
-    }
-    if constexpr (BF16) {
-      // Transpose: element (row j, feature c) goes to Vt[c][vt_pos16(j)].
-      // Each dword of a loaded chunk holds features 2w (low half) and 2w+1.
-      const int pos = vt_pos16(v_row0);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const uint32_t sel = p ? 0x07060302u : 0x05040100u;
-          const int c = v_chunk * 8 + 2 * w + p;
-          char* dst = Vt + c * TL::VROW + pos * 2;
-          if constexpr (TL::VR == 2) {
-            *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-          } else {
-            u32x2 val;
-            val[0] = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel);
-            val[1] = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel);
-            *reinterpret_cast<u32x2*>(dst) = val;
-          }
-        }
-      }
-    } else {
-      // fp32: element (row j, feature c) goes to Vt[c][j]; 4 rows per store.
-#pragma unroll
-      for (int g = 0; g < TL::VR / 4; ++g) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = v_chunk * 4 + e;
-          u32x4 val;
-          val[0] = vreg[4 * g + 0][e];
-          val[1] = vreg[4 * g + 1][e];
-          val[2] = vreg[4 * g + 2][e];
-          val[3] = vreg[4 * g + 3][e];
-          *reinterpret_cast<u32x4*>(Vt + c * TL::VROW + (v_row0 + 4 * g) * 4) = val;
-        }
-      }
-    }
-  };
+  for (int s = 0; s < NQF; ++s) asm volatile("" : : "v"(qf[s]));
 
   // ---- running state: one query row per lane ----
   f32x16 o[D / 32];
@@ -252,14 +207,17 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s
   float l_run = 0.0f;               // this lane's share of the row sum
 
-  if (nkb > 0) {
-    fetch(0);
-    stash();
-  }
+  if (nkb > 0) G::stage(smem, Kp + head_k, Vp + head_k, kv_bytes, 0, 0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 1 < nkb) fetch(kb + 1);
+    const int st = kb & 1;
+    // Block kb+1 goes to the other stage, which every wave finished reading
+    // before the barrier that ended the previous iteration.
+    if (kb + 1 < nkb) G::stage(smem, Kp + head_k, Vp + head_k, kv_bytes, kb + 1, st ^ 1, wave, lane);
+    const char* kt = smem + st * G::STAGE;
+    const char* vt = kt + G::TILE;
 
     if (kb < wave_nkb) {
       // ---- scores: S^T[j][i] for the 64 keys of this block, two 32-key tiles
@@ -268,18 +226,21 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       for (int jt = 0; jt < BC / 32; ++jt) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
-        const char* krow = Ks + (jt * 32 + li) * TL::KROW;
+        const int j = jt * 32 + li;
+        const char* krow = kt + j * G::ROWB;
+        const int sw = G::swz_k(j);
         if constexpr (BF16) {
 #pragma unroll
           for (int ks = 0; ks < D / 16; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(krow + (16 * ks + 8 * hi) * 2);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ((2 * ks + hi) ^ sw) * 16);
             s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), s[jt], 0, 0, 0);
           }
         } else {
 #pragma unroll
           for (int q4 = 0; q4 < D / 8; ++q4) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(krow + (4 * q4 + (D / 2) * hi) * 4);
+            const f32x4 a =
+                *reinterpret_cast<const f32x4*>(krow + ((q4 + (D / 8) * hi) ^ sw) * 16);
             const f32x4 bq = __builtin_bit_cast(f32x4, qf[q4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -292,16 +253,15 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       const int jblk = kb * BC;
       const bool need_mask = (jblk + BC > L) || (CAUSAL && jblk + BC - 1 > row_w);
       if (need_mask) {
+        // valid iff j < key_limit; key offsets within the block are constants
+        const int lim = (CAUSAL ? min(L, my_row + 1) : L) - jblk - 4 * hi;
 #pragma unroll
         for (int jt = 0; jt < BC / 32; ++jt)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = jblk + 32 * jt + 8 * g + 4 * hi + r;
-              const bool ok = (j < L) && (!CAUSAL || j <= my_row);
-              if (!ok) s[jt][4 * g + r] = -__builtin_inff();
-            }
+            for (int r = 0; r < 4; ++r)
+              if (32 * jt + 8 * g + r >= lim) s[jt][4 * g + r] = -__builtin_inff();
       }
 
       // ---- online softmax: block row max, conditional rescale
@@ -310,7 +270,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       for (int jt = 0; jt < BC / 32; ++jt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
-      mx = fmaxf(mx, other_half(mx));
+      mx = pair_max(mx);
       const float mx2 = mx * scale_log2;  // -inf stays -inf (scale_log2 > 0)
       const bool grow = mx2 > m_run + TAU;
       if (__any(grow)) {
@@ -328,10 +288,9 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       // ---- weights p = 2^(s*scale*log2e - m), rounded to T, and PV
       if constexpr (BF16) {
         // Slice k (16 keys, k = 0..3) of this block takes accumulator tile
-        // jt = k/2, groups g = 2(k%2) and 2(k%2)+1: lane half hi then holds
-        // keys 16k + {4hi + r, 8 + 4hi + r}, r = 0..3, as k-slots 8hi..8hi+7,
-        // which is why the V tile is stored with bits 2 and 3 of the key
-        // index swapped.
+        // jt = k/2, groups g = 2(k%2) and 2(k%2)+1: lane half hi holds keys
+        // 16k + 4hi + r (k-slots 8hi + r) and 16k + 8 + 4hi + r (k-slots
+        // 8hi + 4 + r), r = 0..3.
         bf16x8 pf[BC / 16];
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -348,19 +307,36 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
             pf[k][e + 1] = pk[1];
           }
         }
+        // V^T operand through the LDS transpose read: in each 16-lane group
+        // lanes 4k'..4k'+3 read 16 consecutive features of key row k', and
+        // lane t receives feature t of the four rows.  Group gi = lane/16
+        // covers features 16(gi%2)..+15 of the 32-feature tile and keys of
+        // lane half gi/2 (= hi).
+        const int gi = lane / 16, t16 = lane % 16, kr = t16 / 4, qq = t16 % 4;
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) {
-          const char* vrow = Vt + (ct * 32 + li) * TL::VROW;
+          const int cc = ct * 4 + 2 * (gi % 2) + qq / 2;  // 16-byte chunk of the 4 features
 #pragma unroll
           for (int k = 0; k < BC / 16; ++k) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + (16 * k + 8 * hi) * 2);
-            o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[k], o[ct], 0, 0, 0);
+            bf16x8 a;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int row = 16 * k + 8 * half + 4 * hi + kr;
+              const char* p = vt + row * G::ROWB + ((cc ^ G::swz_v(row)) * 16) + (qq % 2) * 8;
+              const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+              const bf16x4 b4 = __builtin_bit_cast(bf16x4, v4);
+              a[4 * half + 0] = b4[0];
+              a[4 * half + 1] = b4[1];
+              a[4 * half + 2] = b4[2];
+              a[4 * half + 3] = b4[3];
+            }
+            o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k], o[ct], 0, 0, 0);
           }
         }
       } else {
         // fp32: one MFMA per accumulator element; k-slot hi of the step
-        // (jt, g, r) is key 32jt + 8g + 4hi + r, read from the natural-order
-        // transposed V tile.
+        // (jt, g, r) is key 32jt + 8g + 4hi + r, read as a single element of
+        // the row-major V tile.
 #pragma unroll
         for (int jt = 0; jt < BC / 32; ++jt)
 #pragma unroll
@@ -371,27 +347,30 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
           }
 #pragma unroll
         for (int ct = 0; ct < D / 32; ++ct) {
-          const char* vrow = Vt + (ct * 32 + li) * TL::VROW;
+          const int c = ct * 32 + li;
 #pragma unroll
           for (int jt = 0; jt < BC / 32; ++jt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const f32x4 a = *reinterpret_cast<const f32x4*>(vrow + (32 * jt + 8 * g + 4 * hi) * 4);
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                o[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[r], s[jt][4 * g + r], o[ct], 0, 0, 0);
-            }
+              for (int r = 0; r < 4; ++r) {
+                const int row = 32 * jt + 8 * g + 4 * hi + r;
+                const float a = *reinterpret_cast<const float*>(
+                    vt + row * G::ROWB + (((c / 4) ^ G::swz_v(row)) * 16) + (c % 4) * 4);
+                o[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, s[jt][4 * g + r], o[ct], 0, 0, 0);
+              }
         }
       }
     }
 
-    __syncthreads();
-    if (kb + 1 < nkb) stash();
+    // This thread's direct loads of block kb+1 have landed; after the
+    // barrier every wave's have, and every wave is done with stage st.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
   // ---- epilogue: divide by the row sum (0 when no key was valid), store
-  const float l_tot = l_run + other_half(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = (l_tot > 0.0f) ? (1.0f / l_tot) : 0.0f;
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct)
