@@ -50,7 +50,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -117,22 +116,30 @@ struct Geo {
   // fills LDS bytes [1 KiB * (u * kWaves + wave), +1 KiB) of each tile; lane
   // t writes the 16 bytes at +16t, i.e. chunk position pc of row r, which
   // holds global chunk pc ^ swizzle(r).  Rows at or beyond `bytes` read as 0.
-  __device__ static inline void stage(char* smem, const T* kbase, const T* vbase, uint32_t bytes,
-                                      int kb, int st, int wave, int lane) {
+  //
+  // The loads are issued from inline assembly (M0 set in the same statement)
+  // so that the compiler's wait-count pass does not treat every later LDS
+  // read as a possible reader of this stage and wait for the loads there;
+  // the kernel waits for them explicitly before the barrier that publishes
+  // the stage.
+  __device__ static inline void stage(uint32_t lds_base, const T* kbase, const T* vbase,
+                                      uint32_t bytes, int kb, int st, int wave, int lane) {
     const auto rk = make_rsrc(kbase, bytes);
     const auto rv = make_rsrc(vbase, bytes);
-    char* kt = smem + st * STAGE;
-    char* vt = kt + TILE;
+    const uint32_t kt = lds_base + st * STAGE;
+    const uint32_t vt = kt + TILE;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int slot = (u * kWaves + wave) * 64;  // first chunk of this load
       const int q = slot + lane;
       const int r = q / CPR, pc = q % CPR;
       const uint32_t row_off = ((uint32_t)(kb * BC + r) * D) * ES;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(kt + slot * 16), 16,
-                                               row_off + (pc ^ swz_k(r)) * 16, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(vt + slot * 16), 16,
-                                               row_off + (pc ^ swz_v(r)) * 16, 0, 0, 0);
+      const uint32_t koff = row_off + (pc ^ swz_k(r)) * 16;
+      const uint32_t voff = row_off + (pc ^ swz_v(r)) * 16;
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(kt + slot * 16), "v"(koff), "s"(rk) : "memory");
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(vt + slot * 16), "v"(voff), "s"(rv) : "memory");
     }
   }
 };
@@ -146,6 +153,8 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   constexpr int ES = G::ES;
   constexpr bool BF16 = G::BF16;
   __shared__ __attribute__((aligned(1024))) char smem[G::LDS_BYTES];
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -207,15 +216,15 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   float m_run = -__builtin_inff();  // running max of scale*log2(e)*s
   float l_run = 0.0f;               // this lane's share of the row sum
 
-  if (nkb > 0) G::stage(smem, Kp + head_k, Vp + head_k, kv_bytes, 0, 0, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (nkb > 0) G::stage(lds_base, Kp + head_k, Vp + head_k, kv_bytes, 0, 0, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int kb = 0; kb < nkb; ++kb) {
     const int st = kb & 1;
     // Block kb+1 goes to the other stage, which every wave finished reading
     // before the barrier that ended the previous iteration.
-    if (kb + 1 < nkb) G::stage(smem, Kp + head_k, Vp + head_k, kv_bytes, kb + 1, st ^ 1, wave, lane);
+    if (kb + 1 < nkb) G::stage(lds_base, Kp + head_k, Vp + head_k, kv_bytes, kb + 1, st ^ 1, wave, lane);
     const char* kt = smem + st * G::STAGE;
     const char* vt = kt + G::TILE;
 
@@ -365,7 +374,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 
     // This thread's direct loads of block kb+1 have landed; after the
     // barrier every wave's have, and every wave is done with stage st.
-    __builtin_amdgcn_s_waitcnt(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
