@@ -22,7 +22,5 @@ struct LaunchArgs {
 };
 
 hipError_t launch_attention(const LaunchArgs& a);
-int query_rows_per_block();
-int keys_per_block();
 
 }  // namespace mha
