@@ -204,6 +204,22 @@ struct Phase {
     }
   }
 
+  // Schedule of the score MFMAs: keep the K operand reads four MFMAs ahead
+  // of their use (the compiler's own schedule issues them about two ahead,
+  // which leaves the MFMAs waiting on LDS latency).
+  MHA_INLINE void prefetch_k() {
+    if constexpr (BF16) {
+      constexpr int NM = NS * (D / 16);  // score MFMAs = K operand reads
+      constexpr int AHEAD = 4;
+      __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (i + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  }
+
   // -inf where the key is invalid.  The lane holds keys
   // 32jt + 8g + 4hi + r of the block; `lim` is the first invalid key of the
   // row minus the block's first key minus 4hi.
@@ -393,6 +409,7 @@ struct Walk {
     if (kb + 1 < wave_nkb) {
       f32x16 s[NS];
       P::scores(s, k_tile(kb + 1), qf, li, hi);
+      P::prefetch_k();
       if (needs_mask(kb + 1)) P::mask(s, row_lim - (kb + 1) * BC - 4 * hi);
       P::pv(o, v_tile(kb), pf_cur, lane);
       bool grew;
@@ -470,6 +487,21 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const T* kbase = Kp + head_k;
   const T* vbase = Vp + head_k;
 
+  // Loads of key block j and value block j into their ring slots.
+  auto load_k = [&](int j) {
+    G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
+  };
+  auto load_v = [&](int j) {
+    G::template stage<false>(lds_v + (j % G::NSTAGE) * G::TILE, vbase, kv_bytes, j, wave, lane);
+  };
+
+  // The first key/value blocks are requested before Q so that their memory
+  // latency overlaps the Q loads.
+  if (nkb > 0) {
+    for (int j = 0; j <= DIST && j < nkb; ++j) load_k(j);
+    for (int j = 0; j < DIST && j < nkb; ++j) load_v(j);
+  }
+
   // ---- Q fragments (MFMA B operand of S^T = K Q^T), kept in registers ----
   // bf16: slice s covers features 16s..16s+15, lane holds 8 of them.
   // fp32: step s pairs feature s (lanes 0-31) with feature D/2 + s (lanes 32-63).
@@ -490,14 +522,6 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   w.m_run = -__builtin_inff();
   w.l_run = 0.0f;
 
-  // Loads of key block j and value block j into their ring slots.
-  auto load_k = [&](int j) {
-    G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
-  };
-  auto load_v = [&](int j) {
-    G::template stage<false>(lds_v + (j % G::NSTAGE) * G::TILE, vbase, kv_bytes, j, wave, lane);
-  };
-
   // Pipeline: iteration kb reads K(kb+1) and V(kb).  It issues the loads of
   // K(kb+1+DIST) and V(kb+DIST), which go to the ring slots of K(kb) and
   // V(kb-1), both last read before the barrier that ended iteration kb-1.
@@ -506,8 +530,6 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // unrolled by two.
   typename P::PFrag pa, pb;
   if (nkb > 0) {
-    for (int j = 0; j <= DIST && j < nkb; ++j) load_k(j);
-    for (int j = 0; j < DIST && j < nkb; ++j) load_v(j);
     G::template wait_loads<0>();
     __syncthreads();
     if (0 < w.wave_nkb) w.first_block(pa);
