@@ -60,6 +60,13 @@ def _load():
         lib.mha_oracle_rows_f64.argtypes = [dp, dp, dp, ip, ctypes.c_int, ctypes.c_double,
                                             i64, i64, i64, i64, i64, i64, lp, i64, dp]
         lib.mha_oracle_rows_f64.restype = ctypes.c_int
+        lib.mha_oracle_ex_f64.argtypes = [dp, dp, dp, ip, ctypes.c_int, dp, ctypes.c_double,
+                                          i64, i64, i64, i64, i64, i64, i64, dp, dp, dp, dp]
+        lib.mha_oracle_ex_f64.restype = ctypes.c_int
+        lib.mha_oracle_ex_rows_f64.argtypes = [dp, dp, dp, ip, ctypes.c_int, dp,
+                                               ctypes.c_double, i64, i64, i64, i64, i64, i64,
+                                               i64, lp, i64, dp, dp]
+        lib.mha_oracle_ex_rows_f64.restype = ctypes.c_int
         lib.mha_oracle_threads.argtypes = []
         lib.mha_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -151,6 +158,97 @@ def attention_rows(q, k, v, rows, key_lens=None, causal=False, scale=None):
     return out
 
 
+_MODES = {False: 0, None: 0, "none": 0, True: 1, "top_left": 1, "bottom_right": 2}
+
+
+def _mode(causal) -> int:
+    if causal not in _MODES:
+        raise ValueError("causal must be False, True, 'top_left' or 'bottom_right'")
+    return _MODES[causal]
+
+
+def _slopes(alibi_slopes, H):
+    if alibi_slopes is None:
+        return None
+    sl = to_f64(alibi_slopes).reshape(-1)
+    if sl.shape != (H,):
+        raise ValueError("alibi_slopes must have H entries")
+    return np.ascontiguousarray(sl)
+
+
+def _ex_shapes(Q, K, V):
+    B, H, n, dk = Q.shape
+    Bk, Hkv, m, dk2 = K.shape
+    dv = V.shape[3]
+    if (Bk, dk2) != (B, dk) or V.shape != (B, Hkv, m, dv):
+        raise ValueError("shape mismatch")
+    return B, H, Hkv, n, m, dk, dv
+
+
+def attention_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None,
+                 scale=None, return_lse=False, return_weights=False):
+    """The extended definition: grouped K/V heads, ALiBi, causal alignment.
+
+    q [B,H,n,dk]; k [B,Hkv,m,dk] and v [B,Hkv,m,dv] with H % Hkv == 0 (query
+    head t reads K/V head t // (H // Hkv)).  causal: False, True or
+    'top_left' (key j visible when j <= i), or 'bottom_right' (when
+    j <= i + L_b - n).  alibi_slopes: H values or None; the scaled score of
+    (i, j) gets -slope * |p_i - j|, p_i = i (+ L_b - n for bottom_right).
+    Returns O [B,H,n,dv] in fp64, then LSE [B,H,n] (natural log, -inf for a
+    row with no valid key) if return_lse, then S and A [B,H,n,m] if
+    return_weights.
+    """
+    Q, K, V = to_f64(q), to_f64(k), to_f64(v)
+    B, H, Hkv, n, m, dk, dv = _ex_shapes(Q, K, V)
+    kl = _lens(key_lens, B)
+    sl = _slopes(alibi_slopes, H)
+    sc = _default_scale(dk) if scale is None else float(scale)
+    O = np.zeros((B, H, n, dv), np.float64)
+    LSE = np.zeros((B, H, n), np.float64) if return_lse else None
+    S = A = None
+    if return_weights:
+        S = np.zeros((B, H, n, m), np.float64)
+        A = np.zeros((B, H, n, m), np.float64)
+    d = ctypes.c_double
+    rc = _load().mha_oracle_ex_f64(
+        _ptr(Q, d), _ptr(K, d), _ptr(V, d),
+        None if kl is None else _ptr(kl, ctypes.c_int32), _mode(causal),
+        None if sl is None else _ptr(sl, d), sc, B, H, Hkv, n, m, dk, dv, _ptr(O, d),
+        None if LSE is None else _ptr(LSE, d), None if S is None else _ptr(S, d),
+        None if A is None else _ptr(A, d))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    out = (O,)
+    if return_lse:
+        out += (LSE,)
+    if return_weights:
+        out += (S, A)
+    return out if len(out) > 1 else O
+
+
+def attention_ex_rows(q, k, v, rows, key_lens=None, causal=False,
+                      alibi_slopes=None, scale=None):
+    """attention_ex for selected rows: rows int [R, 3] of (b, head, i).
+    Returns (O_rows [R, dv], LSE_rows [R]) in fp64."""
+    Q, K, V = to_f64(q), to_f64(k), to_f64(v)
+    B, H, Hkv, n, m, dk, dv = _ex_shapes(Q, K, V)
+    idx = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    kl = _lens(key_lens, B)
+    sl = _slopes(alibi_slopes, H)
+    sc = _default_scale(dk) if scale is None else float(scale)
+    out = np.zeros((idx.shape[0], dv), np.float64)
+    lse = np.zeros((idx.shape[0],), np.float64)
+    d = ctypes.c_double
+    rc = _load().mha_oracle_ex_rows_f64(
+        _ptr(Q, d), _ptr(K, d), _ptr(V, d),
+        None if kl is None else _ptr(kl, ctypes.c_int32), _mode(causal),
+        None if sl is None else _ptr(sl, d), sc, B, H, Hkv, n, m, dk, dv,
+        _ptr(idx, ctypes.c_int64), idx.shape[0], _ptr(out, d), _ptr(lse, d))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out, lse
+
+
 def threads() -> int:
     """OpenMP threads the oracle runs on in this process."""
     return int(_load().mha_oracle_threads())
@@ -160,5 +258,5 @@ def library_path() -> str:
     return _LIB
 
 
-__all__ = ["attention", "attention_rows", "threads", "build", "to_f64",
-           "library_path"]
+__all__ = ["attention", "attention_rows", "attention_ex", "attention_ex_rows",
+           "threads", "build", "to_f64", "library_path"]

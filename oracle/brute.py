@@ -13,21 +13,28 @@ from __future__ import annotations
 import mpmath
 
 
-def attention_row(q, K, V, valid, scale, dps=50):
+def _exps(q, K, valid, scale, bias):
+    sc = mpmath.mpf(scale)
+    e = []
+    for j in range(len(K)):
+        if not valid[j]:
+            e.append(mpmath.mpf(0))
+            continue
+        dot = mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b) for a, b in zip(q, K[j]))
+        s = sc * dot + (mpmath.mpf(bias[j]) if bias is not None else 0)
+        e.append(mpmath.exp(s))
+    return e
+
+
+def attention_row(q, K, V, valid, scale, dps=50, bias=None):
     """One query row.  q: list[d_k]; K: list[m][d_k]; V: list[m][d_v];
-    valid: list[bool] of length m.  Returns (weights list[m], out list[d_v])
-    as mpmath numbers."""
+    valid: list[bool] of length m; bias: None or list[m] added to the scaled
+    scores (ALiBi).  Returns (weights list[m], out list[d_v]) as mpmath
+    numbers."""
     with mpmath.workdps(dps):
-        sc = mpmath.mpf(scale)
         m = len(K)
         dv = len(V[0]) if m else 0
-        e = []
-        for j in range(m):
-            if not valid[j]:
-                e.append(mpmath.mpf(0))
-                continue
-            dot = mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(b) for a, b in zip(q, K[j]))
-            e.append(mpmath.exp(sc * dot))
+        e = _exps(q, K, valid, scale, bias)
         z = mpmath.fsum(e)
         if z == 0:
             return [mpmath.mpf(0)] * m, [mpmath.mpf(0)] * dv
@@ -35,6 +42,14 @@ def attention_row(q, K, V, valid, scale, dps=50):
         out = [mpmath.fsum(w[j] * mpmath.mpf(V[j][c]) for j in range(m))
                for c in range(dv)]
         return w, out
+
+
+def row_logsumexp(q, K, valid, scale, dps=50, bias=None):
+    """log(sum_j exp(s_j)) over the valid keys of one row, as a float, or
+    None when no key is valid."""
+    with mpmath.workdps(dps):
+        z = mpmath.fsum(_exps(q, K, valid, scale, bias))
+        return None if z == 0 else float(mpmath.log(z))
 
 
 def attention(Q, K, V, key_lens=None, causal=False, scale=1.0, dps=50):
