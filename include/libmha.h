@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MHA_ABI_VERSION 1
+#define MHA_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum {
@@ -64,7 +64,15 @@ enum {
     MHA_ERR_SCALE = 5,       /* scale not finite or not > 0 */
     MHA_ERR_ALIAS = 6,       /* O overlaps Q, K, V or key_lens */
     MHA_ERR_HIP = 7,         /* the HIP runtime refused the launch */
-    MHA_ERR_ALIGN = 8        /* a tensor pointer is not 16-byte aligned */
+    MHA_ERR_ALIGN = 8,       /* a tensor pointer is not 16-byte aligned (lse, slopes: 4) */
+    MHA_ERR_MODE = 9         /* mask_mode is not one of the MHA_MASK_* values */
+};
+
+/* Mask modes of the extended entry points (key padding always applies). */
+enum {
+    MHA_MASK_NONE = 0,               /* no causal mask */
+    MHA_MASK_CAUSAL = 1,             /* top-left: key j visible to query i when j <= i */
+    MHA_MASK_CAUSAL_BOTTOM_RIGHT = 2 /* query i is the token at position i + L_b - n */
 };
 
 /* Element types. */
@@ -107,6 +115,79 @@ int mha_forward(const void *Q, const void *K, const void *V,
                 const int32_t *key_lens, int causal, float scale, void *O,
                 int64_t B, int64_t H, int64_t n, int64_t m,
                 int64_t d_k, int64_t d_v, int dtype, void *stream);
+
+/*
+ * ---- Extended forward pass -------------------------------------------------
+ *
+ * The same operation with the variants that sit next to it on the pages:
+ *
+ *     O[b,t,i,:] = sum_j softmax_j( scale * <Q[b,t,i,:], K[b,g,j,:]>
+ *                                   - slope_t * |p_i - j| + M_bij ) * V[b,g,j,:]
+ *
+ *   - Grouped K/V heads (GQA; MQA when H_kv = 1; "Transformer 架构完全指南",
+ *     attention-optimisation table): K and V have H_kv heads and query head
+ *     t reads K/V head g = t / (H / H_kv).  H_kv = H is plain multi-head
+ *     attention.
+ *   - ALiBi ("第2章：完整的 Transformer 架构" §5.3): a per-head slope times
+ *     the query-key distance is subtracted from the scaled score.
+ *     alibi_slopes: device fp32[H], or NULL for no bias.
+ *   - Causal alignment, mask_mode:
+ *       MHA_MASK_NONE                 valid = j < L_b,                p_i = i
+ *       MHA_MASK_CAUSAL               valid = j < L_b and j <= i,     p_i = i
+ *       MHA_MASK_CAUSAL_BOTTOM_RIGHT  valid = j < L_b and j <= p_i,   p_i = i + L_b - n
+ *     Bottom-right places the n queries at the end of a sequence whose first
+ *     L_b keys are filled: incremental decoding against a key/value cache
+ *     of capacity m ("Transformer 架构完全指南", KV-cache section).  Rows with
+ *     no visible key (p_i < 0) have output 0.  Both causal modes accept
+ *     n != m.
+ *   - lse: device fp32[B, H, n] or NULL.  When given, receives each row's
+ *     natural-log log-sum-exp of its valid scaled, biased scores (-inf for a
+ *     row with no valid key); mha_attention_weights consumes it.
+ *
+ * Layout: Q [B, H, n, d_k], K [B, H_kv, m, d_k], V [B, H_kv, m, d_v],
+ * O [B, H, n, d_v], row-major.  Ownership and errors as for mha_forward;
+ * H % H_kv != 0 or H_kv = 0 with H > 0 is MHA_ERR_SHAPE, a bad mask_mode
+ * MHA_ERR_MODE, lse overlapping any other argument MHA_ERR_ALIAS.  Slopes
+ * are device data and are not validated.
+ */
+int mha_validate_ex(const void *Q, const void *K, const void *V,
+                    const int32_t *key_lens, int mask_mode,
+                    const float *alibi_slopes, float scale, const void *O,
+                    const float *lse, int64_t B, int64_t H, int64_t H_kv,
+                    int64_t n, int64_t m, int64_t d_k, int64_t d_v, int dtype);
+
+int mha_forward_ex(const void *Q, const void *K, const void *V,
+                   const int32_t *key_lens, int mask_mode,
+                   const float *alibi_slopes, float scale, void *O, float *lse,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                   int64_t d_k, int64_t d_v, int dtype, void *stream);
+
+/*
+ * ---- Attention weights --------------------------------------------------------
+ *
+ * Writes A[b,t,i,j] = exp(scale * <Q[b,t,i,:], K[b,g,j,:]> - slope_t*|p_i - j|
+ * - lse[b,t,i]) for valid (i, j) and 0 elsewhere: the softmax weights that
+ * the pages' attention function returns beside its output
+ * ("序列建模架构的演进与变革（二）" §4.9).  lse must come from mha_forward_ex
+ * with the same Q, K, key_lens, mask_mode, alibi_slopes and scale.  A is a
+ * dense row-major [B, H, n, m] tensor of the element type `dtype` (16-byte
+ * aligned), fully overwritten; it must not overlap any input.  This pass
+ * materialises B*H*n*m elements, the n x m memory the fused forward pass
+ * avoids; it is for callers that need the weights themselves.  d_k in
+ * {64, 128}; one head's A must stay under 2 GiB.  Errors as for
+ * mha_forward_ex.
+ */
+int mha_validate_weights(const void *Q, const void *K, const int32_t *key_lens,
+                         int mask_mode, const float *alibi_slopes, float scale,
+                         const float *lse, const void *A, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                         int dtype);
+
+int mha_attention_weights(const void *Q, const void *K, const int32_t *key_lens,
+                          int mask_mode, const float *alibi_slopes, float scale,
+                          const float *lse, void *A, int64_t B, int64_t H,
+                          int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                          int dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,15 +21,16 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = mha.header_functions()
     assert set(names) == {"mha_abi_version", "mha_status_string", "mha_validate",
-                          "mha_forward"}
+                          "mha_forward", "mha_validate_ex", "mha_forward_ex",
+                          "mha_validate_weights", "mha_attention_weights"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mha_abi_version() == 1
+    assert lib.mha_abi_version() == 2
 
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(9):
+    for s in range(10):
         txt = lib.mha_status_string(s).decode()
         assert txt and txt not in seen
         seen.add(txt)
@@ -115,3 +116,81 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mha, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         mha.load()
+
+
+# --- extended forward and weights ------------------------------------------------
+
+LSE, SL, A = 0x60000000, 0x70000000, 0x80000000
+MODE = 9
+
+
+def val_ex(lib, q=Q, k=K, v=V, kl=None, mode=0, sl=None, scale=0.125, o=O, lse=None,
+           B=2, H=8, Hkv=8, n=128, m=128, dk=64, dv=64, dtype=BF16):
+    return lib.mha_validate_ex(q, k, v, kl, mode, sl, scale, o, lse, B, H, Hkv, n, m, dk, dv,
+                               dtype)
+
+
+def val_w(lib, q=Q, k=K, kl=None, mode=0, sl=None, scale=0.125, lse=LSE, a=A,
+          B=2, H=8, Hkv=8, n=128, m=128, dk=64, dtype=BF16):
+    return lib.mha_validate_weights(q, k, kl, mode, sl, scale, lse, a, B, H, Hkv, n, m, dk,
+                                    dtype)
+
+
+def test_valid_extended_arguments(lib):
+    assert val_ex(lib) == OK
+    assert val_ex(lib, Hkv=1, mode=2, n=1, m=4096, sl=SL, lse=LSE, kl=KL) == OK
+    assert val_ex(lib, Hkv=2, mode=1, n=100, m=300) == OK   # top-left accepts n != m here
+    assert val_ex(lib, m=0, k=None, v=None, lse=LSE) == OK
+    assert val_w(lib) == OK
+    assert val_w(lib, Hkv=4, mode=2, n=3, m=1000, sl=SL, kl=KL) == OK
+    assert val_w(lib, m=0, k=None, a=None) == OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), SHAPE), (dict(Hkv=0), SHAPE), (dict(Hkv=-1), SHAPE), (dict(Hkv=16), SHAPE),
+    (dict(mode=3), MODE), (dict(mode=-1), MODE),
+    (dict(lse=O + 64), ALIAS), (dict(lse=Q), ALIAS), (dict(lse=KL, kl=KL), ALIAS),
+    (dict(sl=O), ALIAS), (dict(sl=LSE, lse=LSE), ALIAS),
+    (dict(lse=LSE + 2), ALIGN), (dict(sl=SL + 1), ALIGN),
+    (dict(scale=0.0), SCALE), (dict(dk=96, dv=96), UNSUP), (dict(k=None), NULL),
+])
+def test_each_extended_error_status(lib, kw, status):
+    assert val_ex(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=3), SHAPE), (dict(mode=5), MODE), (dict(lse=None), NULL), (dict(a=None), NULL),
+    (dict(a=Q), ALIAS), (dict(a=LSE - 64), ALIAS), (dict(a=K + 16), ALIAS),
+    (dict(a=A + 8), ALIGN), (dict(lse=LSE + 1), ALIGN),
+    (dict(n=1 << 16, m=1 << 16), UNSUP), (dict(dtype=7), DTYPE),
+])
+def test_each_weights_error_status(lib, kw, status):
+    assert val_w(lib, **kw) == status
+
+
+def test_extended_calls_reject_on_host(lib):
+    st = lib.mha_forward_ex(Q, K, V, None, 4, None, 0.125, O, None, 1, 2, 2, 8, 8, 64, 64,
+                            BF16, None)
+    assert st == MODE
+    st = lib.mha_attention_weights(Q, K, None, 0, None, 0.125, LSE, Q, 1, 2, 2, 8, 8, 64,
+                                   BF16, None)
+    assert st == ALIAS
+    assert lib.mha_attention_weights(Q, K, None, 0, None, 0.125, LSE, A, 1, 2, 2, 8, 0, 64,
+                                     BF16, None) == OK
+
+
+def test_binding_mask_modes():
+    assert mha.mask_mode(False) == 0 and mha.mask_mode(True) == 1
+    assert mha.mask_mode("top_left") == 1 and mha.mask_mode("bottom_right") == 2
+    with pytest.raises(ValueError):
+        mha.mask_mode("upper")
+
+
+def test_binding_validate_ex_uses_library_check():
+    import torch
+    q = torch.zeros(1, 4, 16, 64, dtype=torch.bfloat16)
+    k = torch.zeros(1, 2, 17, 64, dtype=torch.bfloat16)
+    out = torch.zeros(1, 4, 16, 64, dtype=torch.bfloat16)
+    assert mha.validate_ex(q, k, k, causal="bottom_right", out=out) == OK
+    k3 = torch.zeros(1, 3, 17, 64, dtype=torch.bfloat16)
+    assert mha.validate_ex(q, k3, k3, out=out) == SHAPE

@@ -1,0 +1,185 @@
+"""GPU parity of the extended entry points against the CPU oracle.
+
+mha_forward_ex (grouped K/V heads, ALiBi, top-left and bottom-right causal
+alignment, log-sum-exp output) and mha_attention_weights, called through the
+C ABI via the binding, on seeded inputs the oracle also receives.
+
+Tolerances (max-abs over every compared element):
+  O       1e-5 (fp32), 1.5e-2 (bf16): as for the core operation.
+  lse     2e-5 (fp32); 3e-3 (bf16): the kernel's row sum adds the weights
+          after rounding them to bf16 (relative error <= 2^-9 each), so
+          |d ln l| <= 2^-9 ~ 1.95e-3, plus fp32 rounding of the scores.
+  A       2e-5 (fp32); 5e-3 (bf16): A <= 1 is stored in bf16 (half an ulp
+          <= 2^-9 ~ 1.95e-3) and carries the lse error above (<= 3e-3 * A).
+Masked weights must be exactly 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_head_scaled_fwd_amd as mha
+from transformer_head_scaled_fwd_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"f32": 1e-5, "bf16": 1.5e-2}
+TOL_LSE = {"f32": 2e-5, "bf16": 3e-3}
+TOL_A = {"f32": 2e-5, "bf16": 5e-3}
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def slopes(H):
+    """Geometric per-head slopes 2^(-8(t+1)/H), the usual ALiBi choice."""
+    return np.array([2.0 ** (-8.0 * (t + 1) / H) for t in range(H)], np.float32)
+
+
+def draw(B, H, Hkv, n, m, d, dt, seed, lens=None):
+    """Q with H heads, K/V with Hkv heads, from the shared generator."""
+    q, _, _, kl = inputs.draw(B, H, n, 1, d, d, dt, seed=seed, lens=None)
+    _, k, v, kl = inputs.draw(B, Hkv, 1, m, d, d, dt, seed=seed + 7919, lens=lens)
+    return q, k, v, kl
+
+
+def gpu_ex(q, k, v, kl, causal, sl, scale=None, weights=False):
+    dl = lambda t: None if t is None else torch.as_tensor(t).to(DEV)  # noqa: E731
+    res = mha.forward_ex(q.to(DEV), k.to(DEV), v.to(DEV), key_lens=dl(kl), causal=causal,
+                         alibi_slopes=dl(sl), scale=scale, return_lse=True,
+                         need_weights=weights)
+    torch.cuda.synchronize()
+    return [r.cpu() for r in res]
+
+
+def maxerr(got, ref, what):
+    g = oracle.to_f64(got)
+    both_inf = np.isneginf(g) & np.isneginf(ref)
+    err = np.where(both_inf, 0.0, np.abs(g - ref))
+    mx = float(err.max()) if err.size else 0.0
+    where = np.unravel_index(np.argmax(err), err.shape) if err.size else ()
+    _say("%s max_abs_err=%.3e at %s" % (what, mx, where))
+    return mx
+
+
+CASES = [
+    # B, H, Hkv, n, m, d, dtype, causal, alibi, lens
+    (2, 8, 2, 300, 300, 64, "bf16", "top_left", False, (1, 300)),
+    (2, 8, 1, 200, 333, 128, "bf16", False, False, (100, 333)),
+    (1, 6, 3, 257, 257, 128, "bf16", "top_left", True, None),
+    (2, 4, 4, 190, 190, 64, "bf16", False, True, (0, 190)),
+    (2, 4, 2, 1, 700, 128, "bf16", "bottom_right", False, (1, 700)),
+    (3, 4, 1, 5, 1000, 64, "bf16", "bottom_right", True, (3, 1000)),
+    (2, 4, 2, 77, 300, 128, "bf16", "bottom_right", True, (50, 300)),
+    (2, 2, 2, 300, 120, 64, "bf16", "bottom_right", False, (10, 120)),
+    (2, 4, 2, 129, 129, 64, "f32", "top_left", True, (1, 129)),
+    (2, 4, 1, 9, 400, 128, "f32", "bottom_right", True, (1, 400)),
+    (1, 2, 2, 100, 250, 64, "f32", False, True, None),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,m,d,dt,causal,alibi,lens", CASES)
+def test_forward_ex_parity(gpu, B, H, Hkv, n, m, d, dt, causal, alibi, lens):
+    _say("case B=%d H=%d Hkv=%d n=%d m=%d d=%d %s causal=%s alibi=%s lens=%s"
+         % (B, H, Hkv, n, m, d, dt, causal, alibi, lens))
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, dt, seed=500 + n + m + d + H, lens=lens)
+    if kl is not None and lens[0] == 0:
+        kl[0] = 0
+    sl = slopes(H) if alibi else None
+    o, lse = gpu_ex(q, k, v, kl, causal, sl)
+    o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal=causal,
+                                         alibi_slopes=sl, scale=mha.default_scale(d),
+                                         return_lse=True)
+    assert torch.isfinite(o.float()).all()
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
+    assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
+
+
+WCASES = [
+    # B, H, Hkv, n, m, d, dtype, causal, alibi, lens
+    (2, 4, 2, 150, 200, 64, "bf16", False, False, (30, 200)),
+    (1, 4, 4, 130, 130, 128, "bf16", "top_left", True, None),
+    (2, 4, 1, 7, 301, 64, "bf16", "bottom_right", True, (5, 301)),
+    (2, 2, 2, 66, 97, 64, "bf16", False, False, None),          # m % 4 != 0
+    (1, 2, 1, 65, 131, 128, "f32", "top_left", False, None),    # m % 4 != 0
+    (2, 2, 2, 40, 120, 64, "f32", "bottom_right", True, (0, 120)),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,m,d,dt,causal,alibi,lens", WCASES)
+def test_attention_weights_parity(gpu, B, H, Hkv, n, m, d, dt, causal, alibi, lens):
+    _say("weights B=%d H=%d Hkv=%d n=%d m=%d d=%d %s causal=%s alibi=%s lens=%s"
+         % (B, H, Hkv, n, m, d, dt, causal, alibi, lens))
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, dt, seed=900 + n + m + d, lens=lens)
+    if kl is not None and lens[0] == 0:
+        kl[0] = 0
+    sl = slopes(H) if alibi else None
+    o, lse, a = gpu_ex(q, k, v, kl, causal, sl, weights=True)
+    o_ref, lse_ref, _, a_ref = oracle.attention_ex(
+        q, k, v, key_lens=kl, causal=causal, alibi_slopes=sl, scale=mha.default_scale(d),
+        return_lse=True, return_weights=True)
+    assert a.dtype == q.dtype and tuple(a.shape) == (B, H, n, m)
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert maxerr(a, a_ref, "A") <= TOL_A[dt]
+    # masked pairs are exactly zero, and nothing else is NaN/Inf
+    a64 = oracle.to_f64(a)
+    assert np.all(a64[a_ref == 0.0] == 0.0)
+    assert np.all(np.isfinite(a64))
+    if dt == "f32":
+        rows = a_ref.sum(-1) > 0
+        np.testing.assert_allclose(a64.sum(-1)[rows], 1.0, atol=1e-5)
+
+
+def test_forward_ex_equals_forward_on_the_core_operation(gpu):
+    # H_kv = H, no bias: the same kernel and the same bits as mha_forward.
+    for causal in (False, True):
+        q, k, v, kl = inputs.draw(2, 4, 200, 200, 64, 64, "bf16", seed=31, lens=(50, 200))
+        qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+        kld = torch.as_tensor(kl).to(DEV)
+        a = mha.forward(qd, kd, vd, key_lens=kld, causal=causal)
+        b = mha.forward_ex(qd, kd, vd, key_lens=kld, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_gqa_equals_repeated_heads_bitwise(gpu):
+    # Reading K/V head t // group is the same computation as repeating the
+    # K/V heads: the outputs agree bit for bit.
+    B, H, Hkv, n, d = 2, 8, 2, 160, 128
+    q, k, v, _ = draw(B, H, Hkv, n, n, d, "bf16", seed=77)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    rep = lambda t: t.repeat_interleave(H // Hkv, dim=1).contiguous()  # noqa: E731
+    a = mha.forward_ex(qd, kd, vd, causal=True)
+    b = mha.forward(qd, rep(kd), rep(vd), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_bottom_right_full_cache_equals_top_left_bitwise(gpu):
+    # With n == m and every key filled the two alignments coincide.
+    q, k, v, _ = inputs.draw(2, 4, 300, 300, 64, 64, "bf16", seed=41, lens=None)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    a = mha.forward_ex(qd, kd, vd, causal="top_left")
+    b = mha.forward_ex(qd, kd, vd, causal="bottom_right")
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_decode_long_cache_sampled_rows(gpu):
+    # One decoding step against a long cache: B=4, H=32 query heads over 8
+    # K/V heads, 4 new tokens each, caches of up to 16384 keys (of capacity
+    # 16384), ALiBi.  The oracle evaluates every output row here.
+    B, H, Hkv, n, m, d = 4, 32, 8, 4, 16384, 128
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, "bf16", seed=2024, lens=(1000, m))
+    kl[0] = m
+    sl = slopes(H)
+    o, lse = gpu_ex(q, k, v, kl, "bottom_right", sl)
+    rows = np.array([[b, t, i] for b in range(B) for t in range(H) for i in range(n)], np.int64)
+    ref, lref = oracle.attention_ex_rows(q, k, v, rows, key_lens=kl, causal="bottom_right",
+                                         alibi_slopes=sl, scale=mha.default_scale(d))
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert maxerr(got, ref, "O") <= TOL_O["bf16"]
+    assert maxerr(lse.reshape(-1), lref, "lse") <= TOL_LSE["bf16"]

@@ -8,6 +8,8 @@ built, every call raises.
 
     import transformer_head_scaled_fwd_amd as mha
     o = mha.forward(q, k, v, key_lens=None, causal=False, scale=None)
+    o, lse, a = mha.forward_ex(q, k, v, causal="bottom_right", alibi_slopes=s,
+                               return_lse=True, need_weights=True)
 
 q [B,H,n,d], k [B,H,m,d], v [B,H,m,d] contiguous bf16 or fp32 tensors on
 one GPU; key_lens an int32 tensor [B] on the same GPU (or None); scale
@@ -59,6 +61,19 @@ def load():
     lib.mha_forward.argtypes = [vp, vp, vp, vp, i32, ctypes.c_float, vp,
                                 i64, i64, i64, i64, i64, i64, i32, vp]
     lib.mha_forward.restype = i32
+    fl = ctypes.c_float
+    lib.mha_validate_ex.argtypes = [vp, vp, vp, vp, i32, vp, fl, vp, vp,
+                                    i64, i64, i64, i64, i64, i64, i64, i32]
+    lib.mha_validate_ex.restype = i32
+    lib.mha_forward_ex.argtypes = [vp, vp, vp, vp, i32, vp, fl, vp, vp,
+                                   i64, i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_forward_ex.restype = i32
+    lib.mha_validate_weights.argtypes = [vp, vp, vp, i32, vp, fl, vp, vp,
+                                         i64, i64, i64, i64, i64, i64, i32]
+    lib.mha_validate_weights.restype = i32
+    lib.mha_attention_weights.argtypes = [vp, vp, vp, i32, vp, fl, vp, vp,
+                                          i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_attention_weights.restype = i32
     _lib = lib
     return lib
 
@@ -157,6 +172,143 @@ def forward(q, k, v, key_lens=None, causal=False, scale=None, out=None, stream=N
     return out
 
 
-__all__ = ["forward", "validate", "load", "abi_version", "status_string",
-           "header_functions", "default_scale", "MhaError", "LIB_PATH",
-           "MHA_F32", "MHA_BF16"]
+MHA_MASK_NONE = 0
+MHA_MASK_CAUSAL = 1
+MHA_MASK_CAUSAL_BOTTOM_RIGHT = 2
+_MODES = {False: MHA_MASK_NONE, None: MHA_MASK_NONE, "none": MHA_MASK_NONE,
+          True: MHA_MASK_CAUSAL, "top_left": MHA_MASK_CAUSAL,
+          "bottom_right": MHA_MASK_CAUSAL_BOTTOM_RIGHT}
+
+
+def mask_mode(causal) -> int:
+    """MHA_MASK_* code of causal = False / True / 'top_left' / 'bottom_right'."""
+    if causal not in _MODES:
+        raise ValueError("causal must be False, True, 'top_left' or 'bottom_right'")
+    return _MODES[causal]
+
+
+def _device_args(q, k, v, key_lens, alibi_slopes):
+    """Checks shared by the extended calls; returns (B, H, Hkv, n, m, dk, dv,
+    dtype code, key_lens ptr, slopes ptr)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or (v is not None and v.dim() != 4):
+        raise ValueError("q, k, v must be 4-D [B, H, L, d]")
+    if q.dtype != k.dtype or (v is not None and v.dtype != q.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    dev = q.device
+    if dev.type != "cuda" or k.device != dev or (v is not None and v.device != dev):
+        raise ValueError("q, k, v must be on the same GPU")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    B, H, n, dk = q.shape
+    Hkv, m = k.shape[1], k.shape[2]
+    dv = v.shape[3] if v is not None else dk
+    if k.shape[0] != B or k.shape[3] != dk or (
+            v is not None and tuple(v.shape[:3]) != (B, Hkv, m)):
+        raise ValueError("shape mismatch: q %s, k %s, v %s" % (
+            tuple(q.shape), tuple(k.shape), None if v is None else tuple(v.shape)))
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != dev or \
+                tuple(key_lens.shape) != (B,) or not key_lens.is_contiguous():
+            raise ValueError("key_lens must be a contiguous int32 tensor [B] on the GPU of q")
+        kl_ptr = key_lens.data_ptr()
+    sl_ptr = None
+    if alibi_slopes is not None:
+        if alibi_slopes.dtype != torch.float32 or alibi_slopes.device != dev or \
+                tuple(alibi_slopes.shape) != (H,) or not alibi_slopes.is_contiguous():
+            raise ValueError("alibi_slopes must be a contiguous float32 tensor [H] on the GPU of q")
+        sl_ptr = alibi_slopes.data_ptr()
+    return B, H, Hkv, n, m, dk, dv, code, kl_ptr, sl_ptr
+
+
+def forward_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=None,
+               return_lse=False, need_weights=False, out=None, stream=None):
+    """The extended forward pass (mha_forward_ex), optionally with the weights.
+
+    k and v may have fewer heads than q (H % H_kv == 0: grouped or
+    multi-query attention).  causal: False, True / 'top_left', or
+    'bottom_right' (queries aligned to the end of each sequence's L_b
+    filled keys, as when decoding against a key/value cache).
+    alibi_slopes: float32 [H] on the GPU, or None.  Returns out, then the
+    fp32 log-sum-exp [B, H, n] if return_lse, then the weights
+    [B, H, n, m] (dtype of q) if need_weights.  Nothing is synchronized.
+    """
+    import torch
+    lib = load()
+    B, H, Hkv, n, m, dk, dv, code, kl_ptr, sl_ptr = _device_args(q, k, v, key_lens,
+                                                                 alibi_slopes)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H, n, dv) or out.dtype != q.dtype or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, n, d_v] tensor like q")
+    lse = None
+    if return_lse or need_weights:
+        lse = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    mode = mask_mode(causal)
+    sc = default_scale(dk) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.mha_forward_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), kl_ptr, mode,
+                                sl_ptr, sc, out.data_ptr(),
+                                None if lse is None else lse.data_ptr(),
+                                B, H, Hkv, n, m, dk, dv, code, stream)
+    _check(st)
+    res = (out,)
+    if return_lse:
+        res += (lse,)
+    if need_weights:
+        res += (attention_weights(q, k, lse, key_lens=key_lens, causal=causal,
+                                  alibi_slopes=alibi_slopes, scale=scale, stream=stream),)
+    return res if len(res) > 1 else out
+
+
+def attention_weights(q, k, lse, key_lens=None, causal=False, alibi_slopes=None,
+                      scale=None, out=None, stream=None):
+    """A[b,t,i,j] = exp(score - lse) on valid pairs, 0 elsewhere
+    (mha_attention_weights); lse from forward_ex with the same arguments."""
+    import torch
+    lib = load()
+    B, H, Hkv, n, m, dk, _, code, kl_ptr, sl_ptr = _device_args(q, k, None, key_lens,
+                                                               alibi_slopes)
+    dev = q.device
+    if lse.dtype != torch.float32 or lse.device != dev or tuple(lse.shape) != (B, H, n) \
+            or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, n] tensor on the GPU of q")
+    if out is None:
+        out = torch.empty((B, H, n, m), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H, n, m) or out.dtype != q.dtype or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, n, m] tensor like q")
+    sc = default_scale(dk) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.mha_attention_weights(q.data_ptr(), k.data_ptr(), kl_ptr, mask_mode(causal),
+                                       sl_ptr, sc, lse.data_ptr(), out.data_ptr(),
+                                       B, H, Hkv, n, m, dk, code, stream)
+    _check(st)
+    return out
+
+
+def validate_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=None,
+                out=None, lse=None) -> int:
+    """The host-side check of mha_forward_ex only; returns the status."""
+    B, H, n, dk = q.shape
+    Hkv, m, dv = k.shape[1], k.shape[2], v.shape[3]
+    sc = default_scale(dk) if scale is None else float(scale)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    return int(load().mha_validate_ex(
+        ptr(q), ptr(k), ptr(v), ptr(key_lens), mask_mode(causal), ptr(alibi_slopes), sc,
+        ptr(out), ptr(lse), B, H, Hkv, n, m, dk, dv, _dtype_code(q)))
+
+
+__all__ = ["forward", "forward_ex", "attention_weights", "validate", "validate_ex",
+           "load", "abi_version", "status_string", "header_functions", "default_scale",
+           "mask_mode", "MhaError", "LIB_PATH", "MHA_F32", "MHA_BF16", "MHA_MASK_NONE",
+           "MHA_MASK_CAUSAL", "MHA_MASK_CAUSAL_BOTTOM_RIGHT"]

@@ -10,6 +10,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmha.so")
 
-SOURCES = ["mha_abi.hip", "mha_fwd_kernel.hip"]
+SOURCES = ["mha_abi.hip", "mha_fwd_kernel.hip", "mha_weights_kernel.hip"]
+OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -30,15 +32,16 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def command(out: str = LIB):
-    return ([hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC]
-            + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out])
+def compile_command(src: str, obj: str):
+    return ([hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"]
+            + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libmha.so; returns its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
+def link_command(objs, out: str = LIB):
+    return [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared"] + list(objs) + ["-o", out]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,6 +53,22 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if msgs and verbose:
         print("\n".join(msgs), file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source (in parallel) and link libmha.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(OBJDIR, s.replace(".hip", ".%s.o" % tag)) for s in SOURCES]
+    try:
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+        tmp = LIB + ".tmp" + tag
+        _run(link_command(objs, tmp), verbose)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     check_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB

@@ -23,6 +23,70 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // head with 32-bit buffer offsets.
 constexpr int64_t kMaxHeadBytes = (int64_t)1 << 31;
 
+// Shared checks of the forward entry points.  H_kv: K/V heads; mode 0/1/2.
+int check_forward(const void* Q, const void* K, const void* V, const int32_t* key_lens, int mode,
+                  const float* alibi, float scale, const void* O, const float* lse, int64_t B,
+                  int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k, int64_t d_v,
+                  int dtype) {
+  if (B < 0 || H < 0 || H_kv < 0 || n < 0 || m < 0 || d_k < 0 || d_v < 0) return MHA_ERR_SHAPE;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_DTYPE;
+  if (mode < MHA_MASK_NONE || mode > MHA_MASK_CAUSAL_BOTTOM_RIGHT) return MHA_ERR_MODE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
+  if (d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
+  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
+  if (n * d_k * es >= kMaxHeadBytes || m * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  const int64_t rows_per_block = 128;
+  const int64_t blocks = ((n + rows_per_block - 1) / rows_per_block) * B * H;
+  if (B > INT32_MAX || H > INT32_MAX || blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  const int64_t q_bytes = B * H * n * d_k * es;
+  const int64_t kv_bytes = B * H_kv * m * d_k * es;
+  const int64_t o_bytes = B * H * n * d_v * es;
+  const int64_t lse_bytes = lse ? B * H * n * 4 : 0;
+  const int64_t alibi_bytes = alibi ? H * 4 : 0;
+  if ((q_bytes > 0 && Q == nullptr) || (kv_bytes > 0 && (K == nullptr || V == nullptr)) ||
+      (o_bytes > 0 && O == nullptr))
+    return MHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return MHA_ERR_ALIGN;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)alibi & 3u)) return MHA_ERR_ALIGN;
+  if (overlaps(O, o_bytes, Q, q_bytes) || overlaps(O, o_bytes, K, kv_bytes) ||
+      overlaps(O, o_bytes, V, kv_bytes) || overlaps(O, o_bytes, key_lens, 4 * B) ||
+      overlaps(O, o_bytes, alibi, alibi_bytes) || overlaps(O, o_bytes, lse, lse_bytes))
+    return MHA_ERR_ALIAS;
+  if (overlaps(lse, lse_bytes, Q, q_bytes) || overlaps(lse, lse_bytes, K, kv_bytes) ||
+      overlaps(lse, lse_bytes, V, kv_bytes) || overlaps(lse, lse_bytes, key_lens, 4 * B) ||
+      overlaps(lse, lse_bytes, alibi, alibi_bytes))
+    return MHA_ERR_ALIAS;
+  return MHA_OK;
+}
+
+int launch_forward(const void* Q, const void* K, const void* V, const int32_t* key_lens,
+                   int mode, const float* alibi, float scale, void* O, float* lse, int64_t B,
+                   int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k, int dtype,
+                   void* stream) {
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  mha::LaunchArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.key_lens = key_lens;
+  a.O = O;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.n = n;
+  a.m = m;
+  a.d = (int)d_k;
+  a.bf16 = dtype == MHA_BF16;
+  a.mode = mode;
+  a.alibi_slopes = alibi;
+  a.lse = lse;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.stream = stream;
+  return mha::launch_attention(a) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -33,14 +97,17 @@ const char* mha_status_string(int s) {
   switch (s) {
     case MHA_OK: return "ok";
     case MHA_ERR_NULL: return "a required pointer is NULL";
-    case MHA_ERR_SHAPE: return "bad shape: negative size, or causal with n != m";
+    case MHA_ERR_SHAPE:
+      return "bad shape: negative size, H not a multiple of H_kv, or causal with n != m";
     case MHA_ERR_DTYPE: return "dtype must be MHA_F32 or MHA_BF16";
     case MHA_ERR_UNSUPPORTED:
       return "unsupported: needs d_k == d_v in {64, 128} and per-head tensors under 2 GiB";
     case MHA_ERR_SCALE: return "scale must be finite and > 0";
-    case MHA_ERR_ALIAS: return "O overlaps Q, K, V or key_lens";
+    case MHA_ERR_ALIAS: return "an output (O, lse or A) overlaps another argument";
     case MHA_ERR_HIP: return "the HIP runtime refused the kernel launch";
-    case MHA_ERR_ALIGN: return "Q, K, V and O must be 16-byte aligned";
+    case MHA_ERR_ALIGN:
+      return "Q, K, V, O (and A) must be 16-byte aligned; lse and alibi_slopes 4-byte aligned";
+    case MHA_ERR_MODE: return "mask_mode must be MHA_MASK_NONE, _CAUSAL or _CAUSAL_BOTTOM_RIGHT";
     default: return "unknown status";
   }
 }
@@ -48,27 +115,9 @@ const char* mha_status_string(int s) {
 int mha_validate(const void* Q, const void* K, const void* V, const int32_t* key_lens,
                  int causal, float scale, const void* O, int64_t B, int64_t H, int64_t n,
                  int64_t m, int64_t d_k, int64_t d_v, int dtype) {
-  if (B < 0 || H < 0 || n < 0 || m < 0 || d_k < 0 || d_v < 0) return MHA_ERR_SHAPE;
-  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_DTYPE;
-  if (causal && n != m) return MHA_ERR_SHAPE;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
-  if (d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
-  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
-  if (n * d_k * es >= kMaxHeadBytes || m * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
-  const int64_t rows_per_block = 128;
-  const int64_t blocks = ((n + rows_per_block - 1) / rows_per_block) * B * H;
-  if (B > INT32_MAX || H > INT32_MAX || blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
-  const int64_t q_bytes = B * H * n * d_k * es;
-  const int64_t kv_bytes = B * H * m * d_k * es;
-  const int64_t o_bytes = B * H * n * d_v * es;
-  if ((q_bytes > 0 && Q == nullptr) || (kv_bytes > 0 && (K == nullptr || V == nullptr)) ||
-      (o_bytes > 0 && O == nullptr))
-    return MHA_ERR_NULL;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return MHA_ERR_ALIGN;
-  if (overlaps(O, o_bytes, Q, q_bytes) || overlaps(O, o_bytes, K, kv_bytes) ||
-      overlaps(O, o_bytes, V, kv_bytes) || overlaps(O, o_bytes, key_lens, 4 * B))
-    return MHA_ERR_ALIAS;
-  return MHA_OK;
+  if (causal && n != m && n >= 0 && m >= 0) return MHA_ERR_SHAPE;
+  return check_forward(Q, K, V, key_lens, causal ? MHA_MASK_CAUSAL : MHA_MASK_NONE, nullptr,
+                       scale, O, nullptr, B, H, H, n, m, d_k, d_v, dtype);
 }
 
 int mha_forward(const void* Q, const void* K, const void* V, const int32_t* key_lens,
@@ -76,23 +125,87 @@ int mha_forward(const void* Q, const void* K, const void* V, const int32_t* key_
                 int64_t d_k, int64_t d_v, int dtype, void* stream) {
   const int st = mha_validate(Q, K, V, key_lens, causal, scale, O, B, H, n, m, d_k, d_v, dtype);
   if (st != MHA_OK) return st;
-  if (B == 0 || H == 0 || n == 0) return MHA_OK;
-  mha::LaunchArgs a;
+  return launch_forward(Q, K, V, key_lens, causal ? MHA_MASK_CAUSAL : MHA_MASK_NONE, nullptr,
+                        scale, O, nullptr, B, H, H, n, m, d_k, dtype, stream);
+}
+
+int mha_validate_ex(const void* Q, const void* K, const void* V, const int32_t* key_lens,
+                    int mask_mode, const float* alibi_slopes, float scale, const void* O,
+                    const float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                    int64_t d_k, int64_t d_v, int dtype) {
+  return check_forward(Q, K, V, key_lens, mask_mode, alibi_slopes, scale, O, lse, B, H, H_kv, n,
+                       m, d_k, d_v, dtype);
+}
+
+int mha_forward_ex(const void* Q, const void* K, const void* V, const int32_t* key_lens,
+                   int mask_mode, const float* alibi_slopes, float scale, void* O, float* lse,
+                   int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                   int64_t d_v, int dtype, void* stream) {
+  const int st = check_forward(Q, K, V, key_lens, mask_mode, alibi_slopes, scale, O, lse, B, H,
+                               H_kv, n, m, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  return launch_forward(Q, K, V, key_lens, mask_mode, alibi_slopes, scale, O, lse, B, H, H_kv, n,
+                        m, d_k, dtype, stream);
+}
+
+int mha_validate_weights(const void* Q, const void* K, const int32_t* key_lens, int mask_mode,
+                         const float* alibi_slopes, float scale, const float* lse,
+                         const void* A, int64_t B, int64_t H, int64_t H_kv, int64_t n,
+                         int64_t m, int64_t d_k, int dtype) {
+  if (B < 0 || H < 0 || H_kv < 0 || n < 0 || m < 0 || d_k < 0) return MHA_ERR_SHAPE;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_DTYPE;
+  if (mask_mode < MHA_MASK_NONE || mask_mode > MHA_MASK_CAUSAL_BOTTOM_RIGHT) return MHA_ERR_MODE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
+  if (d_k != 64 && d_k != 128) return MHA_ERR_UNSUPPORTED;
+  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
+  if (n * d_k * es >= kMaxHeadBytes || m * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  if (n > 0 && m > 0 && n * m * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  const int64_t blocks = ((n + 127) / 128) * B * H;
+  if (B > INT32_MAX || H > INT32_MAX || blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  const int64_t q_bytes = B * H * n * d_k * es;
+  const int64_t k_bytes = B * H_kv * m * d_k * es;
+  const int64_t a_bytes = B * H * n * m * es;
+  const int64_t lse_bytes = B * H * n * 4;
+  const int64_t alibi_bytes = alibi_slopes ? H * 4 : 0;
+  if (a_bytes > 0 && (Q == nullptr || K == nullptr || lse == nullptr || A == nullptr))
+    return MHA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(A)) return MHA_ERR_ALIGN;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)alibi_slopes & 3u)) return MHA_ERR_ALIGN;
+  if (overlaps(A, a_bytes, Q, q_bytes) || overlaps(A, a_bytes, K, k_bytes) ||
+      overlaps(A, a_bytes, key_lens, 4 * B) || overlaps(A, a_bytes, alibi_slopes, alibi_bytes) ||
+      overlaps(A, a_bytes, lse, lse_bytes))
+    return MHA_ERR_ALIAS;
+  return MHA_OK;
+}
+
+int mha_attention_weights(const void* Q, const void* K, const int32_t* key_lens, int mask_mode,
+                          const float* alibi_slopes, float scale, const float* lse, void* A,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                          int64_t d_k, int dtype, void* stream) {
+  const int st = mha_validate_weights(Q, K, key_lens, mask_mode, alibi_slopes, scale, lse, A, B,
+                                      H, H_kv, n, m, d_k, dtype);
+  if (st != MHA_OK) return st;
+  if (B == 0 || H == 0 || n == 0 || m == 0) return MHA_OK;
+  mha::WeightsArgs a;
   a.Q = Q;
   a.K = K;
-  a.V = V;
   a.key_lens = key_lens;
-  a.O = O;
+  a.alibi_slopes = alibi_slopes;
+  a.lse = lse;
+  a.A = A;
   a.B = B;
   a.H = H;
+  a.H_kv = H_kv;
   a.n = n;
   a.m = m;
   a.d = (int)d_k;
   a.bf16 = dtype == MHA_BF16;
-  a.causal = causal != 0;
+  a.mode = mask_mode;
+  a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.stream = stream;
-  return mha::launch_attention(a) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+  return mha::launch_weights(a) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -10,8 +10,13 @@
 //            barrier per block;
 //   scores   S^T = K Q^T on MFMA (32x32 tiles, fp32 accumulate), Q held in
 //            registers for the whole walk;
-//   mask     -inf where j >= L_b or (causal and j > i)
-//            ("Transformer: 详解" §3.4, §5.3);
+//   bias     optional: minus slope_t * |p_i - j| (ALiBi, "第2章：完整的
+//            Transformer 架构" §5.3);
+//   mask     -inf where j >= L_b or (causal and j > p_i)
+//            ("Transformer: 详解" §3.4, §5.3), where the query's position
+//            p_i is i (top-left alignment) or i + L_b - n (bottom-right: the
+//            n queries are the last tokens of a sequence of L_b, as in
+//            decoding against a key/value cache);
 //   softmax  online: running row max and sum in fp32, exp2 with the scale
 //            and log2(e) folded into one FMA, rescale of the output only when
 //            the row max grew by more than 2^TAU ("Transformer" wiki page:
@@ -39,312 +44,22 @@
 // LDS tiles are stored in 16-byte chunks with the chunk index XOR-ed by a
 // function of the row ("swizzle"), chosen per read pattern so that the lanes
 // of one LDS read cycle hit distinct banks.
+//
+// Grouped K/V heads (GQA / MQA, "Transformer 架构完全指南", attention
+// optimisations): query head t reads K/V head t / group.  On request the
+// epilogue also stores each row's log-sum-exp of its scaled, biased, valid
+// scores, from which a second pass can rebuild the weights.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <type_traits>
-
 #include "mha_launch.h"
+#include "mha_tiles.h"
 
 namespace mha {
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRowsPerWave = 32;
-constexpr int BC = 64;  // keys per block
-// The running max used for exp2 is raised only when a row's max exceeds it
-// by more than TAU (log2 units), so unnormalised weights stay below 2^TAU.
-constexpr float TAU = 8.0f;
-// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
-constexpr int kRsrcWord3 = 0x00020000;
-
-#define MHA_INLINE __device__ static inline __attribute__((always_inline))
-#define MHA_MEMBER __device__ inline __attribute__((always_inline))
-
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           kRsrcWord3);
-}
-
-__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
-
-// max / sum of x over lanes l and l^32 (the two lanes that share a query
-// row).  v_permlane32_swap exchanges the upper half of its first operand
-// with the lower half of its second; called with (x, x) each lane receives
-// both its own value and its partner's, in an order that depends on the
-// half, so only symmetric combinations are formed from the pair.
-__device__ inline float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-}
-__device__ inline float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
-}
-
-// LDS swizzles of 16-byte chunks for a row of D elements of type T.
-template <typename T, int D>
-struct Swz {
-  static constexpr bool BF16 = sizeof(T) == 2;
-  static constexpr int CPR = D * (int)sizeof(T) / 16;  // chunks per row: 8, 16 or 32
-  // K is read by rows j = 0..31 of one 16-byte column chunk per MFMA
-  // operand: make the chunk position differ across 16 consecutive rows.
-  __device__ static inline int k(int r) { return CPR == 8 ? ((r >> 1) & 7) : (r & 15); }
-  // V, bf16: the transpose read touches rows 4h..4h+3 x 4 chunks per 32 lanes;
-  // fp32: 32 consecutive elements of rows j and j+4.
-  __device__ static inline int v(int r) {
-    if constexpr (BF16) return CPR == 8 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
-    else return 8 * ((r >> 2) & 1);
-  }
-};
-
-// Tile geometry and LDS ring.  ES: element bytes; NW: waves per workgroup.
-template <typename T, int D, int NW>
-struct Geo {
-  using S = Swz<T, D>;
-  static constexpr int ES = sizeof(T);
-  static constexpr bool BF16 = (ES == 2);
-  static constexpr int BR = kRowsPerWave * NW;  // query rows per workgroup
-  static constexpr int ROWB = D * ES;           // bytes per K or V row in LDS
-  static constexpr int CPR = ROWB / 16;         // chunks per row
-  static constexpr int TILE = BC * ROWB;        // one K or one V block
-  // Two stages: a block is loaded one block ahead of its use.  (A third
-  // stage, loading two blocks ahead, measured slower: the loads already land
-  // within one block's compute, and the ring index costs more.)
-  static constexpr int NSTAGE = 2;
-  static constexpr int DIST = NSTAGE - 1;              // how many blocks ahead loads run
-  static constexpr int LDS_BYTES = NSTAGE * 2 * TILE;  // K ring, then V ring
-  // direct-load instructions per wave for one tile (each moves 1 KiB)
-  static constexpr int LOADS = TILE / 1024 / NW;
-  static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads per wave");
-
-  // Direct loads of one key or value block (block kb, rows at or beyond
-  // `bytes` read as 0) into the tile at LDS address `tile`.  Load u of a
-  // wave fills bytes [1 KiB * (u * NW + wave), +1 KiB) of the tile; lane t
-  // writes the 16 bytes at +16t, i.e. chunk position pc of row r, which
-  // holds global chunk pc ^ swizzle(r).
-  //
-  // The loads are issued from inline assembly (M0 set in the same statement)
-  // so that the compiler's wait-count pass does not treat every later LDS
-  // read as a possible reader of this tile and wait for the loads there;
-  // the kernel waits for them explicitly before the barrier that publishes
-  // the tile.
-  template <bool IS_K>
-  __device__ static inline void stage(uint32_t tile, const T* base, uint32_t bytes, int kb,
-                                      int wave, int lane) {
-    const auto rs = make_rsrc(base, bytes);
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int slot = (u * NW + wave) * 64;  // first chunk of this load
-      const int q = slot + lane;
-      const int r = q / CPR, pc = q % CPR;
-      const uint32_t off =
-          ((uint32_t)(kb * BC + r) * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
-    }
-  }
-
-  // Wait until at most `n` direct loads of this thread are in flight.
-  template <int n>
-  __device__ static inline void wait_loads() {
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(n) : "memory");
-  }
-};
-
-// The phases of one key block for one wave (32 query rows).
-template <typename T, int D>
-struct Phase {
-  using S = Swz<T, D>;
-  static constexpr bool BF16 = sizeof(T) == 2;
-  static constexpr int ROWB = D * (int)sizeof(T);
-  static constexpr int NS = BC / 32;                 // 32-key score tiles per block
-  static constexpr int NQF = BF16 ? D / 16 : D / 8;  // 16-byte Q fragments per lane
-  // P as the PV MFMA consumes it: bf16 slices of 16 keys, or fp32 tiles.
-  using PFrag = std::conditional_t<BF16, bf16x8[BC / 16], f32x16[NS]>;
-
-  // S^T[j][i] for the BC keys of the tile at kt.
-  MHA_INLINE void scores(f32x16 (&s)[NS], const char* kt, const u32x4 (&qf)[NQF], int li, int hi) {
-#pragma unroll
-    for (int jt = 0; jt < NS; ++jt) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
-      const int j = jt * 32 + li;
-      const char* krow = kt + j * ROWB;
-      const int sw = S::k(j);
-      if constexpr (BF16) {
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(krow + ((2 * ks + hi) ^ sw) * 16);
-          s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), s[jt], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int q4 = 0; q4 < D / 8; ++q4) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(krow + ((q4 + (D / 8) * hi) ^ sw) * 16);
-          const f32x4 bq = __builtin_bit_cast(f32x4, qf[q4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[jt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], bq[e], s[jt], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // Schedule of the score MFMAs: keep the K operand reads four MFMAs ahead
-  // of their use (the compiler's own schedule issues them about two ahead,
-  // which leaves the MFMAs waiting on LDS latency).
-  MHA_INLINE void prefetch_k() {
-    if constexpr (BF16) {
-      constexpr int NM = NS * (D / 16);  // score MFMAs = K operand reads
-      constexpr int AHEAD = 4;
-      __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // LDS reads
-#pragma unroll
-      for (int i = 0; i < NM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (i + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-  }
-
-  // -inf where the key is invalid.  The lane holds keys
-  // 32jt + 8g + 4hi + r of the block; `lim` is the first invalid key of the
-  // row minus the block's first key minus 4hi.
-  MHA_INLINE void mask(f32x16 (&s)[NS], int lim) {
-#pragma unroll
-    for (int jt = 0; jt < NS; ++jt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (32 * jt + 8 * g + r >= lim) s[jt][4 * g + r] = -__builtin_inff();
-  }
-
-  // This lane's maximum over its keys of the block (before the pair exchange).
-  MHA_INLINE float lane_max(const f32x16 (&s)[NS]) {
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int jt = 0; jt < NS; ++jt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
-    return mx;
-  }
-
-  // p = 2^(s * scale * log2e - msub), rounded to the PV operand type; the
-  // lane's share of the row sum accumulates the rounded values.
-  //
-  // bf16: slice k (16 keys, k = 0..3) takes tile jt = k/2, groups
-  // g = 2(k%2) and 2(k%2)+1: lane half hi holds keys 16k + 4hi + r (k-slots
-  // 8hi + r) and 16k + 8 + 4hi + r (k-slots 8hi + 4 + r), r = 0..3.
-  MHA_INLINE void weights(PFrag& pf, const f32x16 (&s)[NS], float sl2, float msub, float& l) {
-    if constexpr (BF16) {
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int k = 0; k < BC / 16; ++k) {
-        const int jt = k / 2, g0 = 2 * (k % 2);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int g = g0 + e / 4, r = e % 4;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r], sl2, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r + 1], sl2, -msub));
-          const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
-          pf[k][e] = pk[0];
-          pf[k][e + 1] = pk[1];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int jt = 0; jt < NS; ++jt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][e], sl2, -msub));
-          pf[jt][e] = p;
-          l += p;
-        }
-    }
-  }
-
-  // O^T += V^T P^T for the value tile at vt.
-  MHA_INLINE void pv(f32x16 (&o)[D / 32], const char* vt, const PFrag& pf, int lane) {
-    const int li = lane % 32, hi = lane / 32;
-    if constexpr (BF16) {
-      // V^T operand through the LDS transpose read: in each 16-lane group
-      // lanes 4k'..4k'+3 read 16 consecutive features of key row k', and
-      // lane t receives feature t of the four rows.  Group gi = lane/16
-      // covers features 16(gi%2)..+15 of the 32-feature tile and keys of
-      // lane half gi/2 (= hi).
-      const int gi = lane / 16, t16 = lane % 16, kr = t16 / 4, qq = t16 % 4;
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) {
-        const int cc = ct * 4 + 2 * (gi % 2) + qq / 2;  // 16-byte chunk of the 4 features
-#pragma unroll
-        for (int k = 0; k < BC / 16; ++k) {
-          bf16x8 a;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int row = 16 * k + 8 * half + 4 * hi + kr;
-            const char* p = vt + row * ROWB + ((cc ^ S::v(row)) * 16) + (qq % 2) * 8;
-            const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(p));
-            const bf16x4 b4 = __builtin_bit_cast(bf16x4, v4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[4 * half + e] = b4[e];
-          }
-          o[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[k], o[ct], 0, 0, 0);
-        }
-      }
-    } else {
-      // fp32: one MFMA per accumulator element; k-slot hi of the step
-      // (jt, g, r) is key 32jt + 8g + 4hi + r, read as a single element of
-      // the row-major V tile.
-#pragma unroll
-      for (int ct = 0; ct < D / 32; ++ct) {
-        const int c = ct * 32 + li;
-#pragma unroll
-        for (int jt = 0; jt < NS; ++jt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int row = 32 * jt + 8 * g + 4 * hi + r;
-              const float a = *reinterpret_cast<const float*>(
-                  vt + row * ROWB + (((c / 4) ^ S::v(row)) * 16) + (c % 4) * 4);
-              o[ct] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf[jt][4 * g + r], o[ct], 0, 0, 0);
-            }
-      }
-    }
-  }
-
-  // An empty use of the weights: the compiler must produce them here, which
-  // keeps their computation in the same basic block as the PV MFMAs instead
-  // of sinking it past the rescale branch.
-  MHA_INLINE void pin(const PFrag& pf) {
-    if constexpr (BF16) {
-#pragma unroll
-      for (int k = 0; k < BC / 16; ++k) asm volatile("" : : "v"(pf[k]));
-    } else {
-#pragma unroll
-      for (int jt = 0; jt < NS; ++jt) asm volatile("" : : "v"(pf[jt]));
-    }
-  }
-};
-
 // Per-wave state of the key walk: 32 query rows, one per lane pair.
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
 struct Walk {
   using G = Geo<T, D, NW>;
   using P = Phase<T, D>;
@@ -353,18 +68,20 @@ struct Walk {
   const char* ktiles;  // LDS: K ring, NSTAGE tiles
   const char* vtiles;  // LDS: V ring, NSTAGE tiles
   int lane, li, hi;
-  int row_w;           // first query row of the wave
+  int prow_w;          // position of the first query row of the wave
+  int prow;            // position of this lane's query row
   int row_lim;         // first invalid key of this lane's row
   int L;               // valid keys of the sequence
   int wave_nkb;        // key blocks this wave reads
   float sl2;           // scale * log2(e)
+  float sr;            // ALiBi slope / scale (raw-score units)
   u32x4 qf[P::NQF];    // Q fragments
   f32x16 o[D / 32];    // O^T accumulator
   float m_run;         // running max of scale*log2(e)*s (per row)
   float l_run;         // this lane's share of the row sum
 
   MHA_MEMBER bool needs_mask(int kb) const {
-    return (kb * BC + BC > L) || (CAUSAL && kb * BC + BC - 1 > row_w);
+    return (kb * BC + BC > L) || (CAUSAL && kb * BC + BC - 1 > prow_w);
   }
   MHA_MEMBER const char* k_tile(int kb) const { return ktiles + (kb % G::NSTAGE) * G::TILE; }
   MHA_MEMBER const char* v_tile(int kb) const { return vtiles + (kb % G::NSTAGE) * G::TILE; }
@@ -393,11 +110,17 @@ struct Walk {
   }
   MHA_MEMBER float msub() const { return (m_run == -__builtin_inff()) ? 0.0f : m_run; }
 
+  // Distance bias and mask of block kb's scores.
+  MHA_MEMBER void bias_and_mask(f32x16 (&s)[NS], int kb) const {
+    if constexpr (ALIBI) P::bias(s, (float)(prow - kb * BC - 4 * hi), sr);
+    if (needs_mask(kb)) P::mask(s, row_lim - kb * BC - 4 * hi);
+  }
+
   // Scores, mask, running max and weights of the first block (prologue).
   MHA_MEMBER void first_block(typename P::PFrag& pf) {
     f32x16 s[NS];
     P::scores(s, k_tile(0), qf, li, hi);
-    if (needs_mask(0)) P::mask(s, row_lim - 4 * hi);
+    bias_and_mask(s, 0);
     bool grew;
     raise_max(pair_max(P::lane_max(s)), grew);  // nothing accumulated yet
     P::weights(pf, s, sl2, msub(), l_run);
@@ -410,7 +133,7 @@ struct Walk {
       f32x16 s[NS];
       P::scores(s, k_tile(kb + 1), qf, li, hi);
       P::prefetch_k();
-      if (needs_mask(kb + 1)) P::mask(s, row_lim - (kb + 1) * BC - 4 * hi);
+      bias_and_mask(s, kb + 1);
       P::pv(o, v_tile(kb), pf_cur, lane);
       bool grew;
       const float alpha = raise_max(pair_max(P::lane_max(s)), grew);
@@ -423,13 +146,25 @@ struct Walk {
   }
 };
 
-template <typename T, int D, int NW, bool CAUSAL>
+// Arguments of the forward kernel beyond the tensors.
+struct FwdParams {
+  int H;              // query heads
+  int group;          // query heads per K/V head (H / H_kv)
+  int n, m;           // query rows, key rows per head
+  int nqb;            // query blocks per head
+  int bottom_right;   // causal alignment: 0 top-left, 1 bottom-right
+  float scale;        // the caller's scale
+  float scale_log2;   // scale * log2(e)
+};
+
+template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
 __global__ void __launch_bounds__(64 * NW, 2)
 attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
                 const T* __restrict__ Vp, const int32_t* __restrict__ key_lens,
-                T* __restrict__ Op, int H, int n, int m, int nqb, float scale_log2) {
+                const float* __restrict__ alibi_slopes, T* __restrict__ Op,
+                float* __restrict__ lse, FwdParams prm) {
   using G = Geo<T, D, NW>;
-  using W = Walk<T, D, NW, CAUSAL>;
+  using W = Walk<T, D, NW, CAUSAL, ALIBI>;
   using P = typename W::P;
   constexpr int ES = G::ES;
   constexpr bool BF16 = G::BF16;
@@ -454,11 +189,13 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 
   // Heaviest query blocks first for causal attention: the work of a block
   // grows with its index, so launching them in reverse evens out the tail.
+  const int n = prm.n, m = prm.m, nqb = prm.nqb;
   const int BH = gridDim.x / nqb;
   const int bid = blockIdx.x;
   const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
   const int bh = bid % BH;
-  const int b = bh / H;
+  const int b = bh / prm.H, t = bh % prm.H;
+  const int bkv = b * (prm.H / prm.group) + t / prm.group;  // K/V head
   const int q0 = qb * BR;
 
   int L = m;
@@ -467,20 +204,25 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     L = L < 0 ? 0 : (L > m ? m : L);
   }
   w.L = L;
-  const int kend = CAUSAL ? min(L, q0 + BR) : L;
+  // Position of query row i: i + off.
+  const int off = (CAUSAL && prm.bottom_right) ? L - n : 0;
+  const int kend = CAUSAL ? max(0, min(L, q0 + off + BR)) : L;
   const int nkb = (kend + BC - 1) / BC;
-  w.row_w = q0 + wave * kRowsPerWave;
-  const int my_row = w.row_w + li;
+  const int row_w = q0 + wave * kRowsPerWave;
+  const int my_row = row_w + li;
+  w.prow_w = row_w + off;
+  w.prow = my_row + off;
   // Key blocks any row of this wave can see.
-  w.wave_nkb = CAUSAL ? min(nkb, (w.row_w + kRowsPerWave + BC - 1) / BC) : nkb;
-  w.row_lim = CAUSAL ? min(L, my_row + 1) : L;
-  w.sl2 = scale_log2;
+  w.wave_nkb = CAUSAL ? max(0, min(nkb, (w.prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
+  w.row_lim = CAUSAL ? min(L, my_row + off + 1) : L;
+  w.sl2 = prm.scale_log2;
+  w.sr = ALIBI ? alibi_slopes[t] / prm.scale : 0.0f;
 
   // Buffer resources: out-of-range loads read 0 (also into LDS) and
   // out-of-range stores are dropped, so rows >= n (queries) and >= L (keys,
   // values) need no branch and padded keys are never read from memory.
   const size_t head_q = (size_t)bh * (size_t)n * D;
-  const size_t head_k = (size_t)bh * (size_t)m * D;
+  const size_t head_k = (size_t)bkv * (size_t)m * D;
   const auto rq = make_rsrc(Qp + head_q, (uint32_t)n * D * ES);
   const uint32_t kv_bytes = (uint32_t)L * D * ES;  // rows >= L read as 0
   const auto ro = make_rsrc(Op + head_q, (uint32_t)n * D * ES);
@@ -502,18 +244,8 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     for (int j = 0; j < DIST && j < nkb; ++j) load_v(j);
   }
 
-  // ---- Q fragments (MFMA B operand of S^T = K Q^T), kept in registers ----
-  // bf16: slice s covers features 16s..16s+15, lane holds 8 of them.
-  // fp32: step s pairs feature s (lanes 0-31) with feature D/2 + s (lanes 32-63).
-#pragma unroll
-  for (int s = 0; s < P::NQF; ++s) {
-    uint32_t col = BF16 ? (16 * s + 8 * hi) : (4 * s + (D / 2) * hi);
-    w.qf[s] = load16(rq, ((uint32_t)my_row * D + col) * ES);
-  }
-  // Complete the Q loads here: otherwise the in-order memory counter makes
-  // every iteration of the key loop wait for its own prefetch as well.
-#pragma unroll
-  for (int s = 0; s < P::NQF; ++s) asm volatile("" : : "v"(w.qf[s]));
+  // Q fragments (MFMA B operand of S^T = K Q^T), kept in registers.
+  P::load_q(w.qf, rq, my_row, hi);
 
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -574,6 +306,14 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // ---- epilogue: divide by the row sum (0 when no key was valid), store
   const float l_tot = pair_sum(w.l_run);
   const float inv = (l_tot > 0.0f) ? (1.0f / l_tot) : 0.0f;
+  if (lse != nullptr && hi == 0) {
+    // ln(sum_j exp(scaled score)) = ln 2 * (m_run + log2(l)), m_run in log2 units.
+    const float v = (l_tot > 0.0f) ? 0.6931471805599453f * (w.m_run + __builtin_amdgcn_logf(l_tot))
+                                   : -__builtin_inff();
+    const auto rl = make_rsrc(lse + (size_t)bh * n, (uint32_t)n * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
+                                          (int)((uint32_t)my_row * 4), 0, 0);
+  }
 #pragma unroll
   for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
@@ -593,15 +333,31 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     }
 }
 
-template <typename T, int D, int NW, bool CAUSAL>
+template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
 static hipError_t launch_one(const LaunchArgs& a) {
   constexpr int BR = Geo<T, D, NW>::BR;
-  const int nqb = (int)((a.n + BR - 1) / BR);
-  const int64_t blocks = (int64_t)nqb * a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, CAUSAL>), dim3((unsigned)blocks), dim3(64 * NW), 0,
-                     (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.key_lens,
-                     (T*)a.O, (int)a.H, (int)a.n, (int)a.m, nqb, a.scale_log2);
+  FwdParams prm;
+  prm.H = (int)a.H;
+  prm.group = (int)(a.H / a.H_kv);
+  prm.n = (int)a.n;
+  prm.m = (int)a.m;
+  prm.nqb = (int)((a.n + BR - 1) / BR);
+  prm.bottom_right = a.mode == 2;
+  prm.scale = a.scale;
+  prm.scale_log2 = a.scale_log2;
+  const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, CAUSAL, ALIBI>), dim3((unsigned)blocks),
+                     dim3(64 * NW), 0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K,
+                     (const T*)a.V, a.key_lens, a.alibi_slopes, (T*)a.O, a.lse, prm);
   return hipGetLastError();
+}
+
+template <typename T, int D, int NW>
+static hipError_t launch_variant(const LaunchArgs& a) {
+  const bool causal = a.mode != 0;
+  if (a.alibi_slopes != nullptr)
+    return causal ? launch_one<T, D, NW, true, true>(a) : launch_one<T, D, NW, false, true>(a);
+  return causal ? launch_one<T, D, NW, true, false>(a) : launch_one<T, D, NW, false, false>(a);
 }
 
 // Workgroup size: 8 waves (256 query rows, one workgroup per CU) for bf16
@@ -611,10 +367,9 @@ template <typename T, int D>
 static hipError_t launch_d(const LaunchArgs& a) {
   if constexpr (D == 128 && sizeof(T) == 2) {
     const int64_t big_blocks = ((a.n + 255) / 256) * a.B * a.H;
-    if (big_blocks >= 4 * 256)
-      return a.causal ? launch_one<T, D, 8, true>(a) : launch_one<T, D, 8, false>(a);
+    if (big_blocks >= 4 * 256) return launch_variant<T, D, 8>(a);
   }
-  return a.causal ? launch_one<T, D, 4, true>(a) : launch_one<T, D, 4, false>(a);
+  return launch_variant<T, D, 4>(a);
 }
 
 template <typename T>

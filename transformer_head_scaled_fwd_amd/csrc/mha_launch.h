@@ -13,14 +13,35 @@ struct LaunchArgs {
   const void* V;
   const int32_t* key_lens;  // device int32[B] or nullptr
   void* O;
-  int64_t B, H, n, m;
+  int64_t B, H, H_kv, n, m;  // H % H_kv == 0
   int d;                    // d_k == d_v, 64 or 128
   bool bf16;                // element type: bf16 (true) or fp32 (false)
-  bool causal;
+  int mode;                 // 0 no causal mask, 1 causal top-left, 2 causal bottom-right
+  const float* alibi_slopes;  // device fp32[H] or nullptr
+  float* lse;               // device fp32[B, H, n] or nullptr
+  float scale;              // scale applied to q.k
   float scale_log2;         // scale * log2(e)
   void* stream;             // hipStream_t
 };
 
 hipError_t launch_attention(const LaunchArgs& a);
+
+// Arguments of the weights pass (A = exp(score - lse) over valid pairs).
+struct WeightsArgs {
+  const void* Q;
+  const void* K;
+  const int32_t* key_lens;    // device int32[B] or nullptr
+  const float* alibi_slopes;  // device fp32[H] or nullptr
+  const float* lse;           // device fp32[B, H, n] from the forward pass
+  void* A;                    // device [B, H, n, m], element type of Q
+  int64_t B, H, H_kv, n, m;
+  int d;
+  bool bf16;
+  int mode;
+  float scale, scale_log2;
+  void* stream;
+};
+
+hipError_t launch_weights(const WeightsArgs& a);
 
 }  // namespace mha

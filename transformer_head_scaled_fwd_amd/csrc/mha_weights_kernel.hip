@@ -1,0 +1,222 @@
+// mha_weights_kernel.hip -- the attention weights A as an output, for gfx950.
+//
+// A[b,t,i,j] = exp(scale * q_i.k_j + bias_ij - lse_i) for a valid pair and 0
+// otherwise: the softmax weights that the pages' attention function returns
+// next to its output ("序列建模架构的演进与变革（二）" §4.9, which returns the
+// weight matrix; "Transformer: 详解" §4.1).  lse_i is the row's log-sum-exp,
+// stored by the forward kernel, so one extra pass of score MFMAs rebuilds
+// the normalised weights without a second reduction.
+//
+// Unlike the forward pass this materialises B*H*n*m elements; it is the
+// optional, memory-bound companion of the forward kernel, not part of it.
+//
+// One workgroup (4 waves, 128 query rows) of one (batch, head) walks every
+// key block of the row range: blocks that hold a visible key get S^T = K Q^T
+// on MFMA (K staged through the direct-load ring, one block ahead), the
+// distance bias, the mask and the exponent; blocks past the last visible key
+// are written as zeros without reading K.  Each lane holds one query row and
+// stores 4 consecutive keys at a time.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mha_launch.h"
+#include "mha_tiles.h"
+
+namespace mha {
+
+struct WeightParams {
+  int H, group;          // query heads, query heads per K/V head
+  int n, m;              // query rows, key rows per head
+  int nqb;               // query blocks per head
+  int nkb_all;           // key blocks covering m
+  int bottom_right;      // causal alignment: 0 top-left, 1 bottom-right
+  int vec;               // 1 when m % 4 == 0: four keys per store
+  float scale;           // the caller's scale
+  float scale_log2;      // scale * log2(e)
+};
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+__global__ void __launch_bounds__(256, 2)
+attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
+                    const int32_t* __restrict__ key_lens, const float* __restrict__ alibi_slopes,
+                    const float* __restrict__ lse, T* __restrict__ Ap, WeightParams prm) {
+  constexpr int NW = 4;
+  using G = Geo<T, D, NW>;
+  using P = Phase<T, D>;
+  constexpr int ES = G::ES;
+  constexpr bool BF16 = G::BF16;
+  constexpr int BR = G::BR;
+  constexpr int NS = P::NS;
+  __shared__ __attribute__((aligned(1024))) char smem[G::NSTAGE * G::TILE];
+  const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, li = lane % 32, hi = lane / 32;
+  const int n = prm.n, m = prm.m;
+  const int BH = gridDim.x / prm.nqb;
+  const int bh = blockIdx.x % BH, qb = blockIdx.x / BH;
+  const int b = bh / prm.H, t = bh % prm.H;
+  const int bkv = b * (prm.H / prm.group) + t / prm.group;
+  const int q0 = qb * BR;
+
+  int L = m;
+  if (key_lens != nullptr) {
+    L = key_lens[b];
+    L = L < 0 ? 0 : (L > m ? m : L);
+  }
+  const int off = (CAUSAL && prm.bottom_right) ? L - n : 0;
+  const int kend = CAUSAL ? max(0, min(L, q0 + off + BR)) : L;
+  const int nkb = (kend + BC - 1) / BC;  // blocks with a visible key for some row
+  const int row_w = q0 + wave * kRowsPerWave;
+  const int prow_w = row_w + off;
+  const int wave_nkb = CAUSAL ? max(0, min(nkb, (prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
+  const int my_row = row_w + li;
+  const int prow = my_row + off;
+  const int row_lim = CAUSAL ? min(L, prow + 1) : L;
+  const float sr = ALIBI ? alibi_slopes[t] / prm.scale : 0.0f;
+
+  const auto rq = make_rsrc(Qp + (size_t)bh * n * D, (uint32_t)n * D * ES);
+  const T* kbase = Kp + (size_t)bkv * m * D;
+  const uint32_t kv_bytes = (uint32_t)L * D * ES;
+  // A of this head: rows >= n fall outside the resource and are dropped.
+  const auto ra = make_rsrc(Ap + (size_t)bh * n * m, (uint32_t)((size_t)n * m * ES));
+
+  // log2-domain row constant; a row with no valid key has lse = -inf and
+  // every score masked, so its exponent must not become -inf - -inf.
+  float lse2 = 0.0f;
+  if (my_row < n) {
+    const float v = lse[(size_t)bh * n + my_row];
+    lse2 = (v == -__builtin_inff()) ? 0.0f : v * 1.4426950408889634f;
+  }
+
+  auto load_k = [&](int j) {
+    G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
+  };
+  if (nkb > 0) load_k(0);
+
+  u32x4 qf[P::NQF];
+  P::load_q(qf, rq, my_row, hi);
+
+  // Store the 16 values of score tile jt of block kb (keys
+  // kb*BC + 32jt + 8g + 4hi + r, r = 0..3) for this lane's row.
+  auto store_tile = [&](const f32x16& p, int kb, int jt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int key = kb * BC + 32 * jt + 8 * g + 4 * hi;
+      const uint32_t off_el = (uint32_t)my_row * (uint32_t)m + (uint32_t)key;
+      if (prm.vec) {
+        if (key < m) {
+          if constexpr (BF16) {
+            bf16x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (__bf16)p[4 * g + r];
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ra,
+                                                  (int)(off_el * ES), 0, 0);
+          } else {
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = p[4 * g + r];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ra,
+                                                   (int)(off_el * ES), 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (key + r < m) {
+            if constexpr (BF16) {
+              const __bf16 h = (__bf16)p[4 * g + r];
+              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), ra,
+                                                    (int)((off_el + r) * ES), 0, 0);
+            } else {
+              // (the element is copied out first: a bit cast taken straight
+              // from a vector element reads element 0 of the group here)
+              const float x = p[4 * g + r];
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), ra,
+                                                    (int)((off_el + r) * ES), 0, 0);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  f32x16 zero;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) zero[e] = 0.0f;
+
+  for (int kb = 0; kb < prm.nkb_all; ++kb) {
+    if (kb < nkb) {
+      // K(kb) was requested one block ago; request K(kb+1) into the other
+      // slot (last read before the barrier that ended block kb-1), then wait
+      // for K(kb) only.
+      if (kb + 1 < nkb) {
+        load_k(kb + 1);
+        G::template wait_loads<G::LOADS>();
+      } else {
+        G::template wait_loads<0>();
+      }
+      __syncthreads();
+      if (kb < wave_nkb) {
+        f32x16 s[NS];
+        P::scores(s, smem + (kb % G::NSTAGE) * G::TILE, qf, li, hi);
+        if constexpr (ALIBI) P::bias(s, (float)(prow - kb * BC - 4 * hi), sr);
+        if ((kb * BC + BC > L) || (CAUSAL && kb * BC + BC - 1 > prow_w))
+          P::mask(s, row_lim - kb * BC - 4 * hi);
+#pragma unroll
+        for (int jt = 0; jt < NS; ++jt) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            s[jt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][e], prm.scale_log2, -lse2));
+          store_tile(s[jt], kb, jt);
+        }
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < NS; ++jt) store_tile(zero, kb, jt);
+      }
+      __syncthreads();  // K(kb) is consumed before its slot is refilled
+    } else {
+#pragma unroll
+      for (int jt = 0; jt < NS; ++jt) store_tile(zero, kb, jt);
+    }
+  }
+}
+
+template <typename T, int D, bool CAUSAL, bool ALIBI>
+static hipError_t launch_w(const WeightsArgs& a) {
+  constexpr int BR = Geo<T, D, 4>::BR;
+  WeightParams prm;
+  prm.H = (int)a.H;
+  prm.group = (int)(a.H / a.H_kv);
+  prm.n = (int)a.n;
+  prm.m = (int)a.m;
+  prm.nqb = (int)((a.n + BR - 1) / BR);
+  prm.nkb_all = (int)((a.m + BC - 1) / BC);
+  prm.bottom_right = a.mode == 2;
+  prm.vec = (a.m % 4) == 0;
+  prm.scale = a.scale;
+  prm.scale_log2 = a.scale_log2;
+  const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
+  hipLaunchKernelGGL((attn_weights_kernel<T, D, CAUSAL, ALIBI>), dim3((unsigned)blocks), dim3(256),
+                     0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, a.key_lens,
+                     a.alibi_slopes, a.lse, (T*)a.A, prm);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_wd(const WeightsArgs& a) {
+  const bool causal = a.mode != 0;
+  if (a.alibi_slopes != nullptr)
+    return causal ? launch_w<T, D, true, true>(a) : launch_w<T, D, false, true>(a);
+  return causal ? launch_w<T, D, true, false>(a) : launch_w<T, D, false, false>(a);
+}
+
+hipError_t launch_weights(const WeightsArgs& a) {
+  if (a.bf16) return a.d == 64 ? launch_wd<__bf16, 64>(a) : launch_wd<__bf16, 128>(a);
+  return a.d == 64 ? launch_wd<float, 64>(a) : launch_wd<float, 128>(a);
+}
+
+}  // namespace mha
