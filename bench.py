@@ -10,8 +10,9 @@ the per-launch kernel duration.  Prints ONE JSON line with the headline
 TFLOP/s (4*B*H*n*m*d, halved for causal), a roofline object for the
 kernel, the other workloads (GB/s and TFLOP/s each against its roofline,
 inputs rotated over >= 1 GiB so the 256 MB last-level cache cannot serve
-repeats), and the CPU oracle timed on a bounded sample of the headline
-workload on this host's cores.
+repeats), the workloads of the extended entry points (grouped K/V heads,
+ALiBi, the weights output), and the CPU oracle timed on a bounded sample of
+the headline workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -33,8 +34,8 @@ if _ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix/vector, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-KERNEL_SRC = os.path.join(_ROOT, "transformer_head_scaled_fwd_amd", "csrc",
-                          "mha_fwd_kernel.hip")
+KERNEL_SRCS = [os.path.join(_ROOT, "transformer_head_scaled_fwd_amd", "csrc", f)
+               for f in ("mha_fwd_kernel.hip", "mha_tiles.h")]
 TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "hbm_traffic_causal_n16384_d128.md")
 HEADLINE = "causal_n16384_d128"
 SECONDARY = "encoder_pad_n128"
@@ -61,8 +62,13 @@ def valid_pairs(w, key_lens) -> int:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the forward kernel's sources (the kernel file and the shared
+    device header it includes)."""
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def recorded_traffic():
@@ -166,6 +172,103 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     }, host, sets
 
 
+def visible_keys(n, L, causal):
+    """Visible keys per query row for one sequence with L filled keys."""
+    i = np.arange(n, dtype=np.int64)
+    if causal in (False, None):
+        return np.full(n, L, dtype=np.int64)
+    if causal in (True, "top_left"):
+        return np.minimum(i + 1, L)
+    return np.clip(i + L - n + 1, 0, L)
+
+
+def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+    """One extended workload through mha_forward_ex (plus the weights pass
+    when it asks for them), timed like the core workloads."""
+    from transformer_head_scaled_fwd_amd import inputs
+    w = inputs.EXT_WORKLOADS[name]
+    dev = "cuda:0"
+    q, k, v, kl, sl = inputs.draw_ex(w)
+    q, k, v = q.to(dev), k.to(dev), v.to(dev)
+    kld = None if kl is None else torch.as_tensor(kl).to(dev)
+    sld = None if sl is None else torch.as_tensor(sl).to(dev)
+    es = q.element_size()
+    set_bytes = (q.numel() + k.numel() + v.numel()) * es * 2
+    if w.weights:
+        set_bytes += w.B * w.H * w.n * w.m * es
+    nsets = max(1, min(32, -(-rotate_bytes // max(set_bytes, 1))))
+    sets = [(q, k, v)] + [tuple(torch.roll(t, shifts=s, dims=0).contiguous() + 0
+                                for t in (q, k, v)) for s in range(1, nsets)]
+    outs = [torch.empty((w.B, w.H, w.n, w.d), dtype=q.dtype, device=dev) for _ in sets]
+    lses = [torch.empty((w.B, w.H, w.n), dtype=torch.float32, device=dev) for _ in sets]
+    wts = [torch.empty((w.B, w.H, w.n, w.m), dtype=q.dtype, device=dev) for _ in sets] \
+        if w.weights else None
+    stream = torch.cuda.current_stream()
+
+    def launch(i):
+        j = i % len(sets)
+        a, b, c = sets[j]
+        lib = mha.load()
+        mode = mha.mask_mode(w.causal)
+        st = lib.mha_forward_ex(a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                None if kld is None else kld.data_ptr(), mode,
+                                None if sld is None else sld.data_ptr(), w.scale,
+                                outs[j].data_ptr(), lses[j].data_ptr() if w.weights else None,
+                                w.B, w.H, w.H_kv, w.n, w.m, w.d, w.d,
+                                mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32,
+                                stream.cuda_stream)
+        assert st == 0, st
+        if w.weights:
+            st = lib.mha_attention_weights(a.data_ptr(), b.data_ptr(),
+                                           None if kld is None else kld.data_ptr(), mode,
+                                           None if sld is None else sld.data_ptr(), w.scale,
+                                           lses[j].data_ptr(), wts[j].data_ptr(), w.B, w.H,
+                                           w.H_kv, w.n, w.m, w.d,
+                                           mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32,
+                                           stream.cuda_stream)
+            assert st == 0, st
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern = statistics.mean(per)
+    pairs = 0
+    kv_rows = 0
+    for b in range(w.B):
+        L = w.m if kl is None else int(np.clip(kl[b], 0, w.m))
+        vis = visible_keys(w.n, L, w.causal)
+        pairs += int(vis.sum()) * w.H
+        kv_rows += int(vis.max()) if w.n else 0
+    useful = 4.0 * w.d * pairs
+    abytes = es * (2 * w.B * w.H * w.n * w.d + w.H_kv * kv_rows * 2 * w.d)
+    if w.weights:
+        # the weights pass reads Q and the visible K rows again, writes A
+        abytes += es * (w.B * w.H * w.n * w.d + w.H_kv * kv_rows * w.d +
+                        w.B * w.H * w.n * w.m) + 2 * 4 * w.B * w.H * w.n
+    return {
+        "workload": name, "entry": "mha_forward_ex" + (" + mha_attention_weights"
+                                                       if w.weights else ""),
+        "dtype": w.dtype, "B": w.B, "H": w.H, "H_kv": w.H_kv, "n": w.n, "m": w.m, "d": w.d,
+        "causal": w.causal, "alibi": w.alibi, "key_lens": None if w.lens is None else list(w.lens),
+        "input_sets": len(sets), "launches": steps,
+        "kernel_ms_mean": kern, "kernel_ms_median": statistics.median(per),
+        "kernel_ms_min": min(per),
+        "useful_tflops": useful / (kern * 1e-3) / 1e12,
+        "frac_mfma_peak": useful / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "gbps": abytes / (kern * 1e-3) / 1e9,
+        "frac_hbm": abytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "algorithmic_bytes": abytes, "useful_flops": useful,
+    }
+
+
 def cpu_baseline(w, host, budget_s):
     """The oracle as it stands, on a bounded sample of query rows of the
     headline workload, timed on this host's cores."""
@@ -255,6 +358,12 @@ def main():
             del sets
             others.append(res)
             torch.cuda.empty_cache()
+    ext = []
+    if not args.no_others:
+        for name in inputs.EXT_ORDER:
+            print("bench: %s" % name, file=sys.stderr, flush=True)
+            ext.append(bench_ext(torch, mha, name, 100, 20))
+            torch.cuda.empty_cache()
     traffic = recorded_traffic() if w.name == HEADLINE else None
     cpu = None
     if not args.no_cpu:
@@ -289,6 +398,7 @@ def main():
                      "flops_per_launch": head["metric_flops"]},
         "cpu_baseline": cpu,
         "workloads": [head] + others,
+        "extended": ext,
         "device": device_info(torch),
     }
     print(json.dumps(line), flush=True)

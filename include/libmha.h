@@ -124,10 +124,10 @@ int mha_forward(const void *Q, const void *K, const void *V,
  *     O[b,t,i,:] = sum_j softmax_j( scale * <Q[b,t,i,:], K[b,g,j,:]>
  *                                   - slope_t * |p_i - j| + M_bij ) * V[b,g,j,:]
  *
- *   - Grouped K/V heads (GQA; MQA when H_kv = 1; "Transformer 架构完全指南",
- *     attention-optimisation table): K and V have H_kv heads and query head
- *     t reads K/V head g = t / (H / H_kv).  H_kv = H is plain multi-head
- *     attention.
+ *   - Grouped K/V heads (GQA; MQA when H_kv = 1; hugogu wiki "Transformer",
+ *     attention-optimisation table; "序列建模架构的演进与变革（二）" §3.8):
+ *     K and V have H_kv heads and query head t reads K/V head
+ *     g = t / (H / H_kv).  H_kv = H is plain multi-head attention.
  *   - ALiBi ("第2章：完整的 Transformer 架构" §5.3): a per-head slope times
  *     the query-key distance is subtracted from the scaled score.
  *     alibi_slopes: device fp32[H], or NULL for no bias.
@@ -137,7 +137,7 @@ int mha_forward(const void *Q, const void *K, const void *V,
  *       MHA_MASK_CAUSAL_BOTTOM_RIGHT  valid = j < L_b and j <= p_i,   p_i = i + L_b - n
  *     Bottom-right places the n queries at the end of a sequence whose first
  *     L_b keys are filled: incremental decoding against a key/value cache
- *     of capacity m ("Transformer 架构完全指南", KV-cache section).  Rows with
+ *     of capacity m (hugogu wiki "Transformer", KV-cache section).  Rows with
  *     no visible key (p_i < 0) have output 0.  Both causal modes accept
  *     n != m.
  *   - lse: device fp32[B, H, n] or NULL.  When given, receives each row's

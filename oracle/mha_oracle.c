@@ -33,7 +33,8 @@
  *
  *   - grouped / multi-query attention: Hkv key/value heads shared by groups
  *     of H/Hkv consecutive query heads; query head t reads K/V head
- *     t / (H/Hkv) ("Transformer 架构完全指南" attention-optimisation table:
+ *     t / (H/Hkv) (hugogu wiki "Transformer", attention-optimisation table, and
+ *     "序列建模架构的演进与变革（二）" §3.8:
  *     GQA reduces the number of K/V heads, MQA shares one K/V head among
  *     all queries);
  *   - ALiBi: the scaled score gets -slope_t * |p_i - j| added before the
@@ -43,7 +44,7 @@
  *     decoder mask of "Transformer: 详解" §5.3) or bottom-right (query i is
  *     the token at position p_i = i + L_b - n of a sequence whose first L_b
  *     keys are filled, as in incremental decoding with a key/value cache,
- *     "Transformer 架构完全指南" KV-cache section); without a causal mask
+ *     hugogu wiki "Transformer", KV-cache section); without a causal mask
  *     p_i = i;
  *   - the natural-log log-sum-exp of each row's valid scores (-inf for a
  *     row with no valid key): A_ij = exp(s_ij - lse_i), which is what a

@@ -33,9 +33,7 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def slopes(H):
-    """Geometric per-head slopes 2^(-8(t+1)/H), the usual ALiBi choice."""
-    return np.array([2.0 ** (-8.0 * (t + 1) / H) for t in range(H)], np.float32)
+slopes = inputs.alibi_slopes
 
 
 def draw(B, H, Hkv, n, m, d, dt, seed, lens=None):
@@ -183,3 +181,41 @@ def test_decode_long_cache_sampled_rows(gpu):
     got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
     assert maxerr(got, ref, "O") <= TOL_O["bf16"]
     assert maxerr(lse.reshape(-1), lref, "lse") <= TOL_LSE["bf16"]
+
+
+@pytest.mark.parametrize("name", ["gqa_prefill_n4096", "alibi_causal_n2048"])
+def test_extended_workload_sampled_rows(gpu, name):
+    # The benchmarked extended workloads at full size, in the launch
+    # configuration bench.py times; the oracle evaluates sampled rows.
+    w = inputs.EXT_WORKLOADS[name]
+    _say("extended workload %s (sampled rows)" % name)
+    q, k, v, kl, sl = inputs.draw_ex(w)
+    o, lse = gpu_ex(q, k, v, kl, w.causal, sl, scale=w.scale)
+    rng = np.random.Generator(np.random.PCG64(99))
+    fixed = [0, 1, 63, 64, 127, 128, 255, 256, w.n - 129, w.n - 1]
+    rows = []
+    for b in range(w.B):
+        for t in range(w.H):
+            picks = sorted(set(fixed) | set(rng.integers(0, w.n, 6).tolist()))
+            rows += [[b, t, i] for i in picks]
+    rows = np.array(rows, np.int64)
+    ref, lref = oracle.attention_ex_rows(q, k, v, rows, key_lens=kl, causal=w.causal,
+                                         alibi_slopes=sl, scale=w.scale)
+    got = o[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert maxerr(got, ref, "O") <= TOL_O[w.dtype]
+    gl = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert maxerr(gl, lref, "lse") <= TOL_LSE[w.dtype]
+
+
+def test_weights_workload_full(gpu):
+    w = inputs.EXT_WORKLOADS["weights_n512"]
+    _say("extended workload %s (every element)" % w.name)
+    q, k, v, kl, sl = inputs.draw_ex(w)
+    o, lse, a = gpu_ex(q, k, v, kl, w.causal, sl, scale=w.scale, weights=True)
+    o_ref, lse_ref, _, a_ref = oracle.attention_ex(
+        q, k, v, key_lens=kl, causal=w.causal, alibi_slopes=sl, scale=w.scale,
+        return_lse=True, return_weights=True)
+    assert maxerr(o, o_ref, "O") <= TOL_O[w.dtype]
+    assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[w.dtype]
+    assert maxerr(a, a_ref, "A") <= TOL_A[w.dtype]
+    assert np.all(oracle.to_f64(a)[a_ref == 0.0] == 0.0)

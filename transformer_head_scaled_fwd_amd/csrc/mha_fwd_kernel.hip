@@ -45,10 +45,11 @@
 // function of the row ("swizzle"), chosen per read pattern so that the lanes
 // of one LDS read cycle hit distinct banks.
 //
-// Grouped K/V heads (GQA / MQA, "Transformer 架构完全指南", attention
-// optimisations): query head t reads K/V head t / group.  On request the
-// epilogue also stores each row's log-sum-exp of its scaled, biased, valid
-// scores, from which a second pass can rebuild the weights.
+// Grouped K/V heads (GQA / MQA: hugogu wiki "Transformer", table of
+// attention optimisations; "序列建模架构的演进与变革（二）" §3.8): query head
+// t reads K/V head t / group.  On request the epilogue also stores each
+// row's log-sum-exp of its scaled, biased, valid scores, from which a second
+// pass can rebuild the weights.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

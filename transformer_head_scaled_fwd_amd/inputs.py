@@ -111,3 +111,70 @@ def make(w: Workload):
     """Inputs of a named workload: (q, k, v, key_lens)."""
     return draw(w.B, w.H, w.n, w.m, w.d, w.d, w.dtype, w.seed, w.lens,
                 w.value_scale)
+
+
+# --- workloads of the extended entry points ------------------------------------
+#
+# Grouped K/V heads, ALiBi, bottom-right causal alignment and the weights
+# output.  Same recipe; K and V are drawn with H_kv heads, and ALiBi slopes
+# are the geometric sequence 2^(-8(t+1)/H) over the heads (an input choice:
+# the pages give the slopes only as head-specific constants).
+
+@dataclass(frozen=True)
+class ExtWorkload:
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    n: int
+    m: int
+    d: int
+    dtype: str
+    causal: object                    # False, "top_left" or "bottom_right"
+    lens: Optional[Tuple[int, int]]
+    seed: int
+    alibi: bool = False
+    weights: bool = False
+    value_scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+
+def alibi_slopes(H: int) -> np.ndarray:
+    """fp32 slopes 2^(-8(t+1)/H), t = 0..H-1."""
+    return np.array([2.0 ** (-8.0 * (t + 1) / H) for t in range(H)], np.float32)
+
+
+EXT_WORKLOADS = {
+    "gqa_prefill_n4096": ExtWorkload(
+        "gqa_prefill_n4096", B=2, H=32, H_kv=8, n=4096, m=4096, d=128, dtype="bf16",
+        causal="top_left", lens=None, seed=11,
+        note="causal prefill, 32 query heads over 8 K/V heads"),
+    "alibi_causal_n2048": ExtWorkload(
+        "alibi_causal_n2048", B=8, H=16, H_kv=16, n=2048, m=2048, d=64, dtype="bf16",
+        causal="top_left", lens=None, seed=12, alibi=True,
+        note="causal self-attention with ALiBi"),
+    "weights_n512": ExtWorkload(
+        "weights_n512", B=8, H=8, H_kv=8, n=512, m=512, d=64, dtype="bf16",
+        causal=False, lens=(256, 512), seed=13, weights=True,
+        note="encoder self-attention returning the weights, padding U{256..512}"),
+}
+
+EXT_ORDER = ["gqa_prefill_n4096", "alibi_causal_n2048", "weights_n512"]
+
+
+def draw_ex(w: ExtWorkload, seed_offset: int = 0):
+    """(q, k, v, key_lens, slopes) of an extended workload, on the CPU."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    q = _round(rng.standard_normal((w.B, w.H, w.n, w.d)) * w.value_scale, w.dtype)
+    k = _round(rng.standard_normal((w.B, w.H_kv, w.m, w.d)) * w.value_scale, w.dtype)
+    v = _round(rng.standard_normal((w.B, w.H_kv, w.m, w.d)) * w.value_scale, w.dtype)
+    key_lens = None
+    if w.lens is not None:
+        lo, hi = w.lens
+        key_lens = rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
+    return q, k, v, key_lens, (alibi_slopes(w.H) if w.alibi else None)
+
