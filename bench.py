@@ -205,11 +205,24 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
         if w.weights else None
     stream = torch.cuda.current_stream()
 
+    code = mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32
+    ws_bytes = mha.decode_workspace_size(w.B, w.H, w.H_kv, w.n, w.m, w.d, code) \
+        if w.decode else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
     def launch(i):
         j = i % len(sets)
         a, b, c = sets[j]
         lib = mha.load()
         mode = mha.mask_mode(w.causal)
+        if w.decode:
+            st = lib.mha_decode(a.data_ptr(), b.data_ptr(), c.data_ptr(),
+                                None if kld is None else kld.data_ptr(),
+                                None if sld is None else sld.data_ptr(), w.scale,
+                                outs[j].data_ptr(), None, ws.data_ptr(), ws_bytes,
+                                w.B, w.H, w.H_kv, w.n, w.m, w.d, w.d, code, stream.cuda_stream)
+            assert st == 0, st
+            return
         st = lib.mha_forward_ex(a.data_ptr(), b.data_ptr(), c.data_ptr(),
                                 None if kld is None else kld.data_ptr(), mode,
                                 None if sld is None else sld.data_ptr(), w.scale,
@@ -254,8 +267,9 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
         abytes += es * (w.B * w.H * w.n * w.d + w.H_kv * kv_rows * w.d +
                         w.B * w.H * w.n * w.m) + 2 * 4 * w.B * w.H * w.n
     return {
-        "workload": name, "entry": "mha_forward_ex" + (" + mha_attention_weights"
-                                                       if w.weights else ""),
+        "workload": name, "entry": "mha_decode" if w.decode else (
+            "mha_forward_ex" + (" + mha_attention_weights" if w.weights else "")),
+        "workspace_bytes": ws_bytes,
         "dtype": w.dtype, "B": w.B, "H": w.H, "H_kv": w.H_kv, "n": w.n, "m": w.m, "d": w.d,
         "causal": w.causal, "alibi": w.alibi, "key_lens": None if w.lens is None else list(w.lens),
         "input_sets": len(sets), "launches": steps,

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MHA_ABI_VERSION 2
+#define MHA_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum {
@@ -65,7 +65,8 @@ enum {
     MHA_ERR_ALIAS = 6,       /* O overlaps Q, K, V or key_lens */
     MHA_ERR_HIP = 7,         /* the HIP runtime refused the launch */
     MHA_ERR_ALIGN = 8,       /* a tensor pointer is not 16-byte aligned (lse, slopes: 4) */
-    MHA_ERR_MODE = 9         /* mask_mode is not one of the MHA_MASK_* values */
+    MHA_ERR_MODE = 9,        /* mask_mode is not one of the MHA_MASK_* values */
+    MHA_ERR_WORKSPACE = 10   /* decode workspace missing, too small, misaligned or overlapping */
 };
 
 /* Mask modes of the extended entry points (key padding always applies). */
@@ -188,6 +189,51 @@ int mha_attention_weights(const void *Q, const void *K, const int32_t *key_lens,
                           const float *lse, void *A, int64_t B, int64_t H,
                           int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
                           int dtype, void *stream);
+
+/*
+ * ---- Decoding against a key/value cache ---------------------------------------
+ *
+ * The n new queries of each sequence attend to its cache: K, V [B, H_kv, m, d]
+ * hold the keys and values of the sequence's tokens in rows 0..L_b-1 (the
+ * new tokens' own rows included), m is the cache capacity, L_b =
+ * cache_lens[b] (clamped to [0, m]; NULL means m).  Incremental decoding
+ * stores every earlier token's K and V in a cache allocated at the maximum
+ * length and computes only the new tokens' (hugogu wiki "Transformer",
+ * KV-cache section; "序列建模架构的演进与变革（二）" §3.4).
+ *
+ * The result is exactly that of mha_forward_ex with mask_mode =
+ * MHA_MASK_CAUSAL_BOTTOM_RIGHT and key_lens = cache_lens: query i is the
+ * token at position i + L_b - n.  The difference is the schedule, built for
+ * small n and long caches: the key axis is cut across workgroups so that
+ * the cache streams from HBM at full width even for one sequence.  When it
+ * is cut, the partial results go to a caller-provided workspace and a
+ * second kernel merges them.
+ *
+ * mha_decode_workspace_size: *bytes receives the workspace size the call
+ * with these sizes needs (0 when it needs none).  Pure host arithmetic.
+ *
+ * mha_decode: arguments as for mha_forward_ex (no mask_mode), plus
+ * workspace (device memory of at least that size, 16-byte aligned, not
+ * overlapping any other argument; may be NULL when the size is 0) and its
+ * size.  The workspace holds no state between calls; two calls in flight
+ * at once need two workspaces.  Errors as for mha_forward_ex, and
+ * MHA_ERR_WORKSPACE.
+ */
+int mha_decode_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t n,
+                              int64_t m, int64_t d, int dtype, int64_t *bytes);
+
+int mha_validate_decode(const void *Q, const void *K, const void *V,
+                        const int32_t *cache_lens, const float *alibi_slopes,
+                        float scale, const void *O, const float *lse,
+                        const void *workspace, int64_t workspace_bytes,
+                        int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                        int64_t d_k, int64_t d_v, int dtype);
+
+int mha_decode(const void *Q, const void *K, const void *V,
+               const int32_t *cache_lens, const float *alibi_slopes, float scale,
+               void *O, float *lse, void *workspace, int64_t workspace_bytes,
+               int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+               int64_t d_k, int64_t d_v, int dtype, void *stream);
 
 #ifdef __cplusplus
 }

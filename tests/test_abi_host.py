@@ -22,15 +22,16 @@ def test_exports_every_declared_function(lib):
     names = mha.header_functions()
     assert set(names) == {"mha_abi_version", "mha_status_string", "mha_validate",
                           "mha_forward", "mha_validate_ex", "mha_forward_ex",
-                          "mha_validate_weights", "mha_attention_weights"}
+                          "mha_validate_weights", "mha_attention_weights",
+                          "mha_decode_workspace_size", "mha_validate_decode", "mha_decode"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mha_abi_version() == 2
+    assert lib.mha_abi_version() == 3
 
 
 def test_status_strings(lib):
     seen = set()
-    for s in range(10):
+    for s in range(11):
         txt = lib.mha_status_string(s).decode()
         assert txt and txt not in seen
         seen.add(txt)
@@ -194,3 +195,49 @@ def test_binding_validate_ex_uses_library_check():
     assert mha.validate_ex(q, k, k, causal="bottom_right", out=out) == OK
     k3 = torch.zeros(1, 3, 17, 64, dtype=torch.bfloat16)
     assert mha.validate_ex(q, k3, k3, out=out) == SHAPE
+
+
+# --- decode ----------------------------------------------------------------------
+
+WSPACE = 0x90000000
+WS = 10
+
+
+def ws_size(B=8, H=32, Hkv=8, n=1, m=16384, d=128, dtype=BF16):
+    import ctypes
+    out = ctypes.c_int64(-1)
+    st = mha.load().mha_decode_workspace_size(B, H, Hkv, n, m, d, dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def test_decode_workspace_size():
+    st, big = ws_size()
+    assert st == OK and big > 0
+    # a grid that already fills the device needs no split, hence no workspace
+    st, none = ws_size(B=256, H=32, Hkv=32, m=4096)
+    assert st == OK and none == 0
+    assert ws_size(Hkv=3)[0] == SHAPE
+    assert ws_size(d=96)[0] == UNSUP
+    assert ws_size(B=0) == (OK, 0)
+    # the size grows with the rows that need partial results
+    assert ws_size(n=4)[1] > big
+
+
+def val_dec(lib, ws=WSPACE, wsb=1 << 30, q=Q, k=K, v=V, kl=None, sl=None, o=O, lse=None,
+            B=8, H=32, Hkv=8, n=1, m=16384, d=128, dtype=BF16):
+    return lib.mha_validate_decode(q, k, v, kl, sl, 0.125, o, lse, ws, wsb, B, H, Hkv, n, m,
+                                   d, d, dtype)
+
+
+def test_decode_validation(lib):
+    need = ws_size()[1]
+    assert val_dec(lib, wsb=need) == OK
+    assert val_dec(lib, wsb=need - 1) == WS
+    assert val_dec(lib, ws=None) == WS
+    assert val_dec(lib, ws=WSPACE + 8) == WS
+    assert val_dec(lib, ws=O) == WS                      # overlaps the output
+    assert val_dec(lib, Hkv=5) == SHAPE
+    assert val_dec(lib, B=64, H=32, Hkv=32, m=512, ws=None, wsb=0) == OK
+    st = lib.mha_decode(Q, K, V, None, None, 0.125, O, None, None, 0, 8, 32, 8, 1, 16384,
+                        128, 128, BF16, None)
+    assert st == WS

@@ -1,0 +1,110 @@
+"""GPU parity of mha_decode (few new queries against a key/value cache).
+
+The decode pass must give the result of the extended oracle with
+bottom-right causal alignment and key_lens = cache_lens: query i is the
+token at position i + L_b - n of a cache filled to L_b rows.  Tolerances are
+those of the forward pass (O: 1e-5 fp32, 1.5e-2 bf16; lse: 2e-5 fp32,
+3e-3 bf16, see test_parity_ex_gpu.py for their derivation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_head_scaled_fwd_amd as mha
+from transformer_head_scaled_fwd_amd import inputs
+from test_parity_ex_gpu import TOL_LSE, TOL_O, draw, maxerr
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_decode(q, k, v, kl, sl, scale=None, workspace=None):
+    dl = lambda t: None if t is None else torch.as_tensor(t).to(DEV)  # noqa: E731
+    o, lse = mha.decode(q.to(DEV), k.to(DEV), v.to(DEV), cache_lens=dl(kl),
+                        alibi_slopes=dl(sl), scale=scale, return_lse=True,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+CASES = [
+    # B, H, Hkv, n, m, d, dtype, alibi, lens
+    (4, 32, 8, 1, 4096, 128, "bf16", False, (1000, 4096)),   # split over workgroups
+    (2, 8, 1, 3, 2000, 64, "bf16", True, (1, 2000)),         # MQA, 24 rows, ragged cache
+    (1, 16, 2, 5, 1500, 128, "bf16", False, None),           # 40 rows: two row sets
+    (3, 4, 4, 1, 300, 64, "bf16", True, (0, 300)),           # an empty cache
+    (2, 4, 2, 6, 100, 64, "bf16", False, (3, 100)),          # more queries than keys
+    (64, 16, 16, 1, 256, 64, "bf16", False, (100, 256)),     # no split: direct store
+    (2, 8, 2, 2, 1000, 128, "f32", True, (500, 1000)),
+    (2, 4, 4, 1, 700, 64, "f32", False, None),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,n,m,d,dt,alibi,lens", CASES)
+def test_decode_parity(gpu, B, H, Hkv, n, m, d, dt, alibi, lens):
+    _say("decode B=%d H=%d Hkv=%d n=%d m=%d d=%d %s alibi=%s lens=%s"
+         % (B, H, Hkv, n, m, d, dt, alibi, lens))
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, dt, seed=1300 + n + m + d + H, lens=lens)
+    if kl is not None and lens[0] == 0:
+        kl[0] = 0
+    sl = inputs.alibi_slopes(H) if alibi else None
+    o, lse = run_decode(q, k, v, kl, sl)
+    o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal="bottom_right",
+                                         alibi_slopes=sl, scale=mha.default_scale(d),
+                                         return_lse=True)
+    assert torch.isfinite(o.float()).all()
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
+    assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
+
+
+def test_decode_ignores_workspace_contents_and_padding(gpu):
+    # The workspace carries nothing between calls, and cache rows past L_b
+    # are never read: NaN in either changes no bit of the result.
+    B, H, Hkv, n, m, d = 4, 32, 8, 2, 3000, 128
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, "bf16", seed=1401, lens=(700, 3000))
+    need = mha.decode_workspace_size(B, H, Hkv, n, m, d, mha.MHA_BF16)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    o1, l1 = run_decode(q, k, v, kl, None, workspace=ws)
+    ws.view(torch.float32).fill_(float("nan"))
+    k2, v2 = k.clone(), v.clone()
+    for b in range(B):
+        k2[b, :, kl[b]:] = float("nan")
+        v2[b, :, kl[b]:] = float("nan")
+    o2, l2 = run_decode(q, k2, v2, kl, None, workspace=ws)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = run_decode(q, k, v, kl, None, workspace=ws)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)   # run to run
+
+
+def test_decode_matches_forward_ex(gpu):
+    # The same operation through the prefill-shaped kernel.
+    B, H, Hkv, n, m, d = 2, 16, 4, 3, 1200, 64
+    q, k, v, kl = draw(B, H, Hkv, n, m, d, "bf16", seed=1402, lens=(400, 1200))
+    o_dec, _ = run_decode(q, k, v, kl, None)
+    o_fwd = mha.forward_ex(q.to(DEV), k.to(DEV), v.to(DEV), key_lens=torch.as_tensor(kl).to(DEV),
+                           causal="bottom_right")
+    torch.cuda.synchronize()
+    assert (o_dec.float() - o_fwd.cpu().float()).abs().max().item() <= 2 * TOL_O["bf16"]
+
+
+@pytest.mark.parametrize("name", ["decode_gqa_m16384", "decode_mha_m8192"])
+def test_decode_workload_every_row(gpu, name):
+    # The benchmarked decode workloads at full size, in the launch
+    # configuration bench.py times; every output row against the oracle.
+    w = inputs.EXT_WORKLOADS[name]
+    _say("decode workload %s" % name)
+    q, k, v, kl, sl = inputs.draw_ex(w)
+    o, lse = run_decode(q, k, v, kl, sl, scale=w.scale)
+    rows = np.array([[b, t, i] for b in range(w.B) for t in range(w.H) for i in range(w.n)],
+                    np.int64)
+    ref, lref = oracle.attention_ex_rows(q, k, v, rows, key_lens=kl, causal="bottom_right",
+                                         alibi_slopes=sl, scale=w.scale)
+    assert maxerr(o.reshape(-1, w.d), ref, "O") <= TOL_O[w.dtype]
+    assert maxerr(lse.reshape(-1), lref, "lse") <= TOL_LSE[w.dtype]

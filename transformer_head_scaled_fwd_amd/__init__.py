@@ -74,6 +74,15 @@ def load():
     lib.mha_attention_weights.argtypes = [vp, vp, vp, i32, vp, fl, vp, vp,
                                           i64, i64, i64, i64, i64, i64, i32, vp]
     lib.mha_attention_weights.restype = i32
+    lib.mha_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i32,
+                                              ctypes.POINTER(i64)]
+    lib.mha_decode_workspace_size.restype = i32
+    lib.mha_validate_decode.argtypes = [vp, vp, vp, vp, vp, fl, vp, vp, vp, i64,
+                                        i64, i64, i64, i64, i64, i64, i64, i32]
+    lib.mha_validate_decode.restype = i32
+    lib.mha_decode.argtypes = [vp, vp, vp, vp, vp, fl, vp, vp, vp, i64,
+                               i64, i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_decode.restype = i32
     _lib = lib
     return lib
 
@@ -296,6 +305,50 @@ def attention_weights(q, k, lse, key_lens=None, causal=False, alibi_slopes=None,
     return out
 
 
+def decode_workspace_size(B, H, H_kv, n, m, d, dtype_code) -> int:
+    """Bytes of workspace mha_decode needs for these sizes (0: none)."""
+    out = ctypes.c_int64(0)
+    _check(load().mha_decode_workspace_size(B, H, H_kv, n, m, d, dtype_code, ctypes.byref(out)))
+    return int(out.value)
+
+
+def decode(q, k_cache, v_cache, cache_lens=None, alibi_slopes=None, scale=None,
+           return_lse=False, out=None, workspace=None, stream=None):
+    """n new queries per sequence against a key/value cache (mha_decode).
+
+    q [B, H, n, d]; k_cache, v_cache [B, H_kv, m, d] with m the capacity;
+    cache_lens int32 [B] (filled rows, the new tokens' included) or None.
+    Query i is the token at position i + L_b - n.  A workspace of
+    decode_workspace_size(...) bytes is allocated when none is given.
+    Returns out (and the fp32 log-sum-exp [B, H, n] if return_lse).
+    """
+    import torch
+    lib = load()
+    B, H, Hkv, n, m, dk, dv, code, kl_ptr, sl_ptr = _device_args(q, k_cache, v_cache,
+                                                                 cache_lens, alibi_slopes)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, n, dv), dtype=q.dtype, device=dev)
+    elif out.shape != (B, H, n, dv) or out.dtype != q.dtype or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, H, n, d_v] tensor like q")
+    lse = torch.empty((B, H, n), dtype=torch.float32, device=dev) if return_lse else None
+    need = decode_workspace_size(B, H, Hkv, n, m, dk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    sc = default_scale(dk) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = lib.mha_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), kl_ptr, sl_ptr,
+                            sc, out.data_ptr(), None if lse is None else lse.data_ptr(),
+                            ws_ptr, ws_bytes, B, H, Hkv, n, m, dk, dv, code, stream)
+    _check(st)
+    return (out, lse) if return_lse else out
+
+
 def validate_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=None,
                 out=None, lse=None) -> int:
     """The host-side check of mha_forward_ex only; returns the status."""
@@ -308,7 +361,7 @@ def validate_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=N
         ptr(out), ptr(lse), B, H, Hkv, n, m, dk, dv, _dtype_code(q)))
 
 
-__all__ = ["forward", "forward_ex", "attention_weights", "validate", "validate_ex",
+__all__ = ["forward", "forward_ex", "attention_weights", "decode", "decode_workspace_size", "validate", "validate_ex",
            "load", "abi_version", "status_string", "header_functions", "default_scale",
            "mask_mode", "MhaError", "LIB_PATH", "MHA_F32", "MHA_BF16", "MHA_MASK_NONE",
            "MHA_MASK_CAUSAL", "MHA_MASK_CAUSAL_BOTTOM_RIGHT"]

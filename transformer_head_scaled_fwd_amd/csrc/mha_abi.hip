@@ -108,6 +108,7 @@ const char* mha_status_string(int s) {
     case MHA_ERR_ALIGN:
       return "Q, K, V, O (and A) must be 16-byte aligned; lse and alibi_slopes 4-byte aligned";
     case MHA_ERR_MODE: return "mask_mode must be MHA_MASK_NONE, _CAUSAL or _CAUSAL_BOTTOM_RIGHT";
+    case MHA_ERR_WORKSPACE: return "workspace missing, too small, misaligned or overlapping";
     default: return "unknown status";
   }
 }
@@ -206,6 +207,80 @@ int mha_attention_weights(const void* Q, const void* K, const int32_t* key_lens,
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.stream = stream;
   return mha::launch_weights(a) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+int mha_decode_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                              int64_t d, int dtype, int64_t* bytes) {
+  if (bytes == nullptr) return MHA_ERR_NULL;
+  *bytes = 0;
+  if (B < 0 || H < 0 || H_kv < 0 || n < 0 || m < 0 || d < 0) return MHA_ERR_SHAPE;
+  if (H > 0 && (H_kv == 0 || H % H_kv != 0)) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_DTYPE;
+  if (d != 64 && d != 128) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  *bytes = mha::plan_decode(B, H, H_kv, n, m, (int)d, dtype == MHA_BF16).workspace_bytes;
+  return MHA_OK;
+}
+
+int mha_validate_decode(const void* Q, const void* K, const void* V, const int32_t* cache_lens,
+                        const float* alibi_slopes, float scale, const void* O, const float* lse,
+                        const void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                        int64_t H_kv, int64_t n, int64_t m, int64_t d_k, int64_t d_v,
+                        int dtype) {
+  int st = check_forward(Q, K, V, cache_lens, MHA_MASK_CAUSAL_BOTTOM_RIGHT, alibi_slopes, scale,
+                         O, lse, B, H, H_kv, n, m, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
+  if (H * n * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
+  if (B * H_kv * p.nrs * p.nsplit > INT32_MAX || B * H * n > INT32_MAX)
+    return MHA_ERR_UNSUPPORTED;
+  if (p.workspace_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.workspace_bytes || !aligned16(workspace))
+      return MHA_ERR_WORKSPACE;
+    const int64_t wb = p.workspace_bytes;
+    const int64_t q_bytes = B * H * n * d_k * es;
+    const int64_t kv_bytes = B * H_kv * m * d_k * es;
+    if (overlaps(workspace, wb, Q, q_bytes) || overlaps(workspace, wb, K, kv_bytes) ||
+        overlaps(workspace, wb, V, kv_bytes) || overlaps(workspace, wb, O, q_bytes) ||
+        overlaps(workspace, wb, cache_lens, 4 * B) ||
+        overlaps(workspace, wb, alibi_slopes, alibi_slopes ? 4 * H : 0) ||
+        overlaps(workspace, wb, lse, lse ? 4 * B * H * n : 0))
+      return MHA_ERR_WORKSPACE;
+  }
+  return MHA_OK;
+}
+
+int mha_decode(const void* Q, const void* K, const void* V, const int32_t* cache_lens,
+               const float* alibi_slopes, float scale, void* O, float* lse, void* workspace,
+               int64_t workspace_bytes, int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+               int64_t d_k, int64_t d_v, int dtype, void* stream) {
+  const int st = mha_validate_decode(Q, K, V, cache_lens, alibi_slopes, scale, O, lse, workspace,
+                                     workspace_bytes, B, H, H_kv, n, m, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
+  mha::DecodeArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.cache_lens = cache_lens;
+  a.alibi_slopes = alibi_slopes;
+  a.O = O;
+  a.lse = lse;
+  a.workspace = workspace;
+  a.B = B;
+  a.H = H;
+  a.H_kv = H_kv;
+  a.n = n;
+  a.m = m;
+  a.d = (int)d_k;
+  a.bf16 = dtype == MHA_BF16;
+  a.scale = scale;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.stream = stream;
+  return mha::launch_decode(a, p) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
 }  // extern "C"

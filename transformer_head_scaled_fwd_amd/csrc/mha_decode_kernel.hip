@@ -1,0 +1,329 @@
+// mha_decode_kernel.hip -- attention of a few new queries against a long
+// key/value cache, for gfx950.
+//
+// Incremental decoding keeps the keys and values of every earlier token in a
+// cache allocated at its maximum length and computes only the new tokens'
+// K and V at each step (hugogu wiki "Transformer", KV-cache section;
+// "序列建模架构的演进与变革（二）" §3.4 and §3.8).  The n new queries of
+// sequence b are the last n of its L_b filled keys, so query i sits at
+// position p_i = i + L_b - n and sees keys j <= p_i (bottom-right causal
+// alignment); the result is the same as mha_forward_ex with
+// MHA_MASK_CAUSAL_BOTTOM_RIGHT.
+//
+// The work is a stream over the cache: each cached K/V row is read once for
+// all the query rows that use its head (the group of query heads sharing a
+// K/V head, times the n new tokens: R = group * n rows, up to 32 per wave).
+// The key axis is cut two ways to fill the chip:
+//
+//   - across the waves of a workgroup: wave w takes key blocks w, w+NW, ...
+//     of the workgroup's range, staging each K and V block into its own LDS
+//     tiles (buffer->LDS direct loads, one block in flight per tile) and
+//     running the same score / mask / bias / online-softmax / PV phases as
+//     the forward kernel on its 32 rows;
+//   - across workgroups ("splits"): when the (batch, K/V head) pairs alone
+//     cannot fill the chip, the range is cut into splits whose partial
+//     results (running max m, row sum l, unnormalised O) go to a workspace
+//     and a second, small kernel merges them.
+//
+// Partial results merge by the same rescaling the online softmax uses:
+// with M = max_s m_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mha_launch.h"
+#include "mha_tiles.h"
+
+namespace mha {
+
+struct DecParams {
+  int H, group;          // query heads, query heads per K/V head
+  int n, m;              // new queries per sequence, cache capacity
+  int R;                 // query rows per (batch, K/V head): group * n
+  int nrs;               // row sets of 32 rows: ceil(R / 32)
+  int nsplit;            // workgroups along the key axis
+  int split_blocks;      // key blocks per split (a multiple of the wave count)
+  float scale, scale_log2;
+};
+
+template <typename T, int D, int NW>
+struct DecGeo {
+  using G1 = Geo<T, D, 1>;  // one wave stages a whole tile
+  static constexpr int TILE = G1::TILE;
+  static constexpr int TILES_BYTES = NW * 2 * TILE;                 // K and V tile per wave
+  static constexpr int MERGE_BYTES = NW * kRowsPerWave * (D + 2) * 4;  // O, m, l per wave
+  static constexpr int LDS_BYTES = TILES_BYTES > MERGE_BYTES ? TILES_BYTES : MERGE_BYTES;
+};
+
+template <typename T, int D, int NW, bool ALIBI>
+__global__ void __launch_bounds__(64 * NW, 1)
+attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* __restrict__ Vp,
+                   const int32_t* __restrict__ cache_lens, const float* __restrict__ alibi_slopes,
+                   T* __restrict__ Op, float* __restrict__ lse, float* __restrict__ part_o,
+                   float* __restrict__ part_ml, DecParams prm) {
+  using DG = DecGeo<T, D, NW>;
+  using G1 = typename DG::G1;
+  using P = Phase<T, D>;
+  constexpr int ES = G1::ES;
+  constexpr int NS = P::NS;
+  constexpr int LOADS = G1::LOADS;  // direct loads per tile
+  __shared__ __attribute__((aligned(1024))) char smem[DG::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, li = lane % 32, hi = lane / 32;
+  const int n = prm.n, m = prm.m;
+
+  // grid: ((b * Hkv + g) * nrs + rs) * nsplit + s
+  int bid = blockIdx.x;
+  const int s = bid % prm.nsplit;
+  bid /= prm.nsplit;
+  const int rs = bid % prm.nrs;
+  bid /= prm.nrs;
+  const int Hkv = prm.H / prm.group;
+  const int g = bid % Hkv, b = bid / Hkv;
+
+  int L = m;
+  if (cache_lens != nullptr) {
+    L = cache_lens[b];
+    L = L < 0 ? 0 : (L > m ? m : L);
+  }
+
+  // This lane's query row: r = rs*32 + li -> head t = g*group + r / n,
+  // token i = r % n.  Lanes past R compute a dummy row that is never stored.
+  const int r = rs * kRowsPerWave + li;
+  const bool real = r < prm.R;
+  const int t = g * prm.group + (real ? r / n : 0);
+  const int i = real ? r % n : 0;
+  const int qrow = real ? t * n + i : prm.H * n;  // row within batch b; dummy reads 0
+  const int prow = i + L - n;                     // position of the query
+  const int row_lim = real ? min(L, prow + 1) : L;
+  const int lim_min = L - n + 1;                  // smallest limit of a real row (i = 0)
+
+  const auto rq = make_rsrc(Qp + (size_t)b * prm.H * n * D, (uint32_t)prm.H * n * D * ES);
+  const size_t head_k = ((size_t)b * Hkv + g) * (size_t)m * D;
+  const T* kbase = Kp + head_k;
+  const T* vbase = Vp + head_k;
+  const uint32_t kv_bytes = (uint32_t)L * D * ES;  // rows >= L read as 0
+  const float sl2 = prm.scale_log2;
+  const float sr = ALIBI ? alibi_slopes[t] / prm.scale : 0.0f;
+
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
+  const uint32_t kt_lds = lds_base + wave * 2 * DG::TILE;
+  const uint32_t vt_lds = kt_lds + DG::TILE;
+  const char* ktile = smem + wave * 2 * DG::TILE;
+  const char* vtile = ktile + DG::TILE;
+
+  // Key blocks of this wave: kb = kb0 + wave + NW * k, below kb_end.
+  const int nkb_all = (L + BC - 1) / BC;
+  const int kb0 = s * prm.split_blocks;
+  const int kb_end = min(nkb_all, kb0 + prm.split_blocks);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[ct][e] = 0.0f;
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+
+  int kb = kb0 + wave;
+  if (kb < kb_end) {
+    G1::template stage<true>(kt_lds, kbase, kv_bytes, kb, 0, lane);
+    G1::template stage<false>(vt_lds, vbase, kv_bytes, kb, 0, lane);
+  }
+  u32x4 qf[P::NQF];
+  P::load_q(qf, rq, qrow, hi);
+
+  for (; kb < kb_end; kb += NW) {
+    const bool more = kb + NW < kb_end;
+    // K(kb) then V(kb) were issued; wait for K only.
+    G1::template wait_loads<LOADS>();
+    f32x16 sc[NS];
+    P::scores(sc, ktile, qf, li, hi);
+    // The K tile is free once the score MFMAs have their operands.
+    if (more) G1::template stage<true>(kt_lds, kbase, kv_bytes, kb + NW, 0, lane);
+    if constexpr (ALIBI) P::bias(sc, (float)(prow - kb * BC - 4 * hi), sr);
+    if (kb * BC + BC > lim_min) P::mask(sc, row_lim - kb * BC - 4 * hi);
+    // Online softmax, not thresholded here: one block per step is cheap.
+    const float mx = pair_max(P::lane_max(sc)) * sl2;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
+    typename P::PFrag pf;
+    P::weights(pf, sc, sl2, (m_run == -__builtin_inff()) ? 0.0f : m_run, l_run);
+    // V(kb) was issued before K(kb+NW).
+    if (more) G1::template wait_loads<LOADS>();
+    else G1::template wait_loads<0>();
+    P::pv(o, vtile, pf, lane);
+    if (more) G1::template stage<false>(vt_lds, vbase, kv_bytes, kb + NW, 0, lane);
+  }
+  G1::template wait_loads<0>();
+
+  // ---- merge the waves' partial results through LDS ----
+  const float l_tot = pair_sum(l_run);
+  __syncthreads();  // every wave is done with its tiles
+  float* mo = reinterpret_cast<float*>(smem);  // [NW][32][D]
+  float* mm = mo + NW * kRowsPerWave * D;      // [NW][32]
+  float* ml = mm + NW * kRowsPerWave;          // [NW][32]
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = o[ct][4 * gg + q];
+      *reinterpret_cast<f32x4*>(mo + (wave * kRowsPerWave + li) * D + ct * 32 + 8 * gg + 4 * hi) = v;
+    }
+  if (hi == 0) {
+    mm[wave * kRowsPerWave + li] = m_run;
+    ml[wave * kRowsPerWave + li] = l_tot;
+  }
+  __syncthreads();
+
+  const bool direct = prm.nsplit == 1;
+  const size_t q_batch = (size_t)b * prm.H * n;  // first query row of batch b
+  for (int e = tid; e < kRowsPerWave * D; e += 64 * NW) {
+    const int row = e / D, c = e % D;
+    const int rr = rs * kRowsPerWave + row;
+    if (rr >= prm.R) continue;
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * kRowsPerWave + row]);
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = mm[w * kRowsPerWave + row];
+      const float f = (mw == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+      acc += f * mo[(w * kRowsPerWave + row) * D + c];
+      lsum += f * ml[w * kRowsPerWave + row];
+    }
+    const int tt = g * prm.group + rr / n, ii = rr % n;
+    const size_t orow = q_batch + (size_t)tt * n + ii;  // query row in [B, H, n]
+    if (direct) {
+      const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+      Op[orow * D + c] = (T)(acc * inv);
+      if (c == 0 && lse != nullptr)
+        lse[orow] = (lsum > 0.0f) ? 0.6931471805599453f * (M + __builtin_amdgcn_logf(lsum))
+                                  : -__builtin_inff();
+    } else {
+      const size_t prow_ws = orow * prm.nsplit + s;
+      part_o[prow_ws * D + c] = acc;
+      if (c == 0) {
+        part_ml[2 * prow_ws] = M;
+        part_ml[2 * prow_ws + 1] = lsum;
+      }
+    }
+  }
+}
+
+// Merge of the splits: one wave per query row, lanes over the features.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
+                           T* __restrict__ Op, float* __restrict__ lse, int rows, int nsplit) {
+  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  if (row >= rows) return;
+  const float* ml = part_ml + (size_t)row * nsplit * 2;
+  float M = -__builtin_inff();
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float lsum = 0.0f;
+  float acc[D / 64];
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) acc[u] = 0.0f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = ml[2 * s];
+    const float f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+    lsum += f * ml[2 * s + 1];
+    const float* po = part_o + ((size_t)row * nsplit + s) * D;
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) acc[u] += f * po[lane + 64 * u];
+  }
+  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int u = 0; u < D / 64; ++u) Op[(size_t)row * D + lane + 64 * u] = (T)(acc[u] * inv);
+  if (lane == 0 && lse != nullptr)
+    lse[row] = (lsum > 0.0f) ? 0.6931471805599453f * (M + __builtin_amdgcn_logf(lsum))
+                             : -__builtin_inff();
+}
+
+// Waves per workgroup: four, except fp32 with d = 128, whose tiles allow two.
+template <typename T, int D>
+constexpr int dec_waves() {
+  return (sizeof(T) == 4 && D == 128) ? 2 : 4;
+}
+
+DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int d,
+                       bool bf16) {
+  DecodePlan p;
+  const int nw = (!bf16 && d == 128) ? 2 : 4;
+  const int64_t R = (H / H_kv) * n;
+  p.nrs = (R + kRowsPerWave - 1) / kRowsPerWave;
+  const int64_t nkb = (m + BC - 1) / BC;
+  const int64_t units = B * H_kv * p.nrs;
+  // About four workgroups per CU of a 256-CU device, with at least one key
+  // block per wave in every split.
+  const int64_t target = 1024;
+  int64_t nsplit = units >= target ? 1 : (target + units - 1) / units;
+  const int64_t max_split = (nkb + nw - 1) / nw;
+  if (nsplit > max_split) nsplit = max_split;
+  if (nsplit < 1) nsplit = 1;
+  int64_t sb = (nkb + nsplit - 1) / nsplit;
+  sb = ((sb + nw - 1) / nw) * nw;
+  if (sb < nw) sb = nw;
+  p.split_blocks = sb;
+  p.nsplit = nkb > 0 ? (nkb + sb - 1) / sb : 1;
+  p.workspace_bytes = p.nsplit > 1 ? B * H * n * p.nsplit * ((int64_t)d + 2) * 4 : 0;
+  return p;
+}
+
+template <typename T, int D, bool ALIBI>
+static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
+  constexpr int NW = dec_waves<T, D>();
+  DecParams prm;
+  prm.H = (int)a.H;
+  prm.group = (int)(a.H / a.H_kv);
+  prm.n = (int)a.n;
+  prm.m = (int)a.m;
+  prm.R = (int)(prm.group * a.n);
+  prm.nrs = (int)p.nrs;
+  prm.nsplit = (int)p.nsplit;
+  prm.split_blocks = (int)p.split_blocks;
+  prm.scale = a.scale;
+  prm.scale_log2 = a.scale_log2;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (p.nsplit > 1) {
+    part_o = (float*)a.workspace;
+    part_ml = part_o + (size_t)a.B * a.H * a.n * p.nsplit * D;
+  }
+  const int64_t blocks = a.B * a.H_kv * p.nrs * p.nsplit;
+  hipLaunchKernelGGL((attn_decode_kernel<T, D, NW, ALIBI>), dim3((unsigned)blocks), dim3(64 * NW),
+                     0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, (const T*)a.V,
+                     a.cache_lens, a.alibi_slopes, (T*)a.O, a.lse, part_o, part_ml, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit == 1) return e;
+  const int64_t rows = a.B * a.H * a.n;
+  hipLaunchKernelGGL((attn_decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)),
+                     dim3(256), 0, (hipStream_t)a.stream, part_o, part_ml, (T*)a.O, a.lse,
+                     (int)rows, (int)p.nsplit);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_dec_d(const DecodeArgs& a, const DecodePlan& p) {
+  return a.alibi_slopes ? launch_dec<T, D, true>(a, p) : launch_dec<T, D, false>(a, p);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p) {
+  if (a.bf16) return a.d == 64 ? launch_dec_d<__bf16, 64>(a, p) : launch_dec_d<__bf16, 128>(a, p);
+  return a.d == 64 ? launch_dec_d<float, 64>(a, p) : launch_dec_d<float, 128>(a, p);
+}
+
+}  // namespace mha

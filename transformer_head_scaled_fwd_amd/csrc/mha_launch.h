@@ -44,4 +44,32 @@ struct WeightsArgs {
 
 hipError_t launch_weights(const WeightsArgs& a);
 
+// Arguments of the decode pass (few queries against a key/value cache).
+struct DecodeArgs {
+  const void* Q;              // [B, H, n, d]
+  const void* K;              // [B, H_kv, m, d], m = cache capacity
+  const void* V;
+  const int32_t* cache_lens;  // device int32[B] or nullptr (= m)
+  const float* alibi_slopes;  // device fp32[H] or nullptr
+  void* O;                    // [B, H, n, d]
+  float* lse;                 // device fp32[B, H, n] or nullptr
+  void* workspace;            // DecodePlan::workspace_bytes, or nullptr when 0
+  int64_t B, H, H_kv, n, m;
+  int d;
+  bool bf16;
+  float scale, scale_log2;
+  void* stream;
+};
+
+// How the key axis is cut: row sets of 32 query rows, splits of
+// split_blocks key blocks, and the workspace the splits need (0 when the
+// whole axis fits one workgroup per row set).
+struct DecodePlan {
+  int64_t nrs, nsplit, split_blocks, workspace_bytes;
+};
+
+DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int d,
+                       bool bf16);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p);
+
 }  // namespace mha

@@ -135,6 +135,7 @@ class ExtWorkload:
     seed: int
     alibi: bool = False
     weights: bool = False
+    decode: bool = False              # run through mha_decode (m = cache capacity)
     value_scale: float = 1.0
     note: str = field(default="", compare=False)
 
@@ -161,9 +162,19 @@ EXT_WORKLOADS = {
         "weights_n512", B=8, H=8, H_kv=8, n=512, m=512, d=64, dtype="bf16",
         causal=False, lens=(256, 512), seed=13, weights=True,
         note="encoder self-attention returning the weights, padding U{256..512}"),
+    "decode_gqa_m16384": ExtWorkload(
+        "decode_gqa_m16384", B=8, H=32, H_kv=8, n=1, m=16384, d=128, dtype="bf16",
+        causal="bottom_right", lens=(8192, 16384), seed=14, decode=True,
+        note="one decoding step, 8 sequences, 32 query heads over 8 K/V heads, "
+             "caches of capacity 16384 filled to U{8192..16384}"),
+    "decode_mha_m8192": ExtWorkload(
+        "decode_mha_m8192", B=1, H=32, H_kv=32, n=1, m=8192, d=128, dtype="bf16",
+        causal="bottom_right", lens=None, seed=15, decode=True,
+        note="one decoding step of one sequence with an 8K context, 32 heads of 128"),
 }
 
-EXT_ORDER = ["gqa_prefill_n4096", "alibi_causal_n2048", "weights_n512"]
+EXT_ORDER = ["gqa_prefill_n4096", "alibi_causal_n2048", "weights_n512",
+             "decode_gqa_m16384", "decode_mha_m8192"]
 
 
 def draw_ex(w: ExtWorkload, seed_offset: int = 0):
