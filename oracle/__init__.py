@@ -249,6 +249,48 @@ def attention_ex_rows(q, k, v, rows, key_lens=None, causal=False,
     return out, lse
 
 
+def _linear(x, W, b):
+    """nn.Linear: x W^T + b, W [out, in] (a library matmul in fp64)."""
+    y = np.matmul(x, to_f64(W).T)
+    return y if b is None else y + to_f64(b)
+
+
+def multihead(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H, key_lens=None,
+              causal=False, scale=None, return_weights=False):
+    """Multi-head attention around the core, as the pages write it
+    ("序列建模架构的演进与变革（二）" §4.9, "Transformer: 详解" §4.2,
+    "第2章：完整的 Transformer 架构" §2.2):
+
+      Q = split_heads(xq Wq^T + bq),  K = split_heads(xk Wk^T + bk),
+      V = split_heads(xv Wv^T + bv)          [B, L, d_model] -> [B, H, L, d_k]
+      O = attention(Q, K, V, mask)           per head, the core oracle
+      Y = concat_heads(O) Wo^T + bo          [B, H, n, d_k] -> [B, n, d_model]
+
+    W* are [d_model, d_model] in nn.Linear's [out, in] layout, b* [d_model]
+    or None; d_k = d_model / H.  All fp64, no rounding of intermediates.
+    Returns Y, and with return_weights also A [B, H, n, m].
+    """
+    Xq, Xk, Xv = to_f64(xq), to_f64(xk), to_f64(xv)
+    B, n, dm = Xq.shape
+    m = Xk.shape[1]
+    if dm % H:
+        raise ValueError("d_model must be a multiple of H")
+    dk = dm // H
+
+    def split(x, L):
+        return np.ascontiguousarray(x.reshape(B, L, H, dk).transpose(0, 2, 1, 3))
+
+    Q = split(_linear(Xq, Wq, bq), n)
+    K = split(_linear(Xk, Wk, bk), m)
+    V = split(_linear(Xv, Wv, bv), m)
+    res = attention_ex(Q, K, V, key_lens=key_lens, causal=causal, scale=scale,
+                       return_weights=return_weights)
+    O = res[0] if return_weights else res
+    concat = O.transpose(0, 2, 1, 3).reshape(B, n, dm)
+    Y = _linear(concat, Wo, bo)
+    return (Y, res[2]) if return_weights else Y
+
+
 def threads() -> int:
     """OpenMP threads the oracle runs on in this process."""
     return int(_load().mha_oracle_threads())
@@ -258,5 +300,5 @@ def library_path() -> str:
     return _LIB
 
 
-__all__ = ["attention", "attention_rows", "attention_ex", "attention_ex_rows",
+__all__ = ["attention", "attention_rows", "attention_ex", "attention_ex_rows", "multihead",
            "threads", "build", "to_f64", "library_path"]
