@@ -283,6 +283,71 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     }
 
 
+def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+    """One multi-head layer workload through mha_multihead_forward: the
+    Q/K/V projections, the core and the output projection, timed together
+    with HIP events on the launch stream."""
+    from transformer_head_scaled_fwd_amd import inputs
+    w = inputs.LAYER_WORKLOADS[name]
+    dev = "cuda:0"
+    x, _, _, Ws, bs, kl = inputs.draw_layer(w)
+    x = x.to(dev)
+    Ws = [t.to(dev) for t in Ws]
+    bs = [t.to(dev) for t in bs]
+    kld = None if kl is None else torch.as_tensor(kl).to(dev)
+    es = x.element_size()
+    nsets = max(1, min(32, -(-rotate_bytes // (x.numel() * es * 2))))
+    xs = [x] + [torch.roll(x, shifts=s, dims=0).contiguous() + 0 for s in range(1, nsets)]
+    ys = [torch.empty_like(x) for _ in xs]
+    code = mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32
+    need = mha.multihead_workspace_size(w.B, w.n, w.n, w.d_model, w.H, code)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    lib = mha.load()
+    mode = mha.mask_mode(w.causal)
+    scale = mha.default_scale(w.d_model // w.H)
+
+    def launch(i):
+        j = i % len(xs)
+        p = xs[j].data_ptr()
+        st = lib.mha_multihead_forward(
+            p, p, p, Ws[0].data_ptr(), bs[0].data_ptr(), Ws[1].data_ptr(), bs[1].data_ptr(),
+            Ws[2].data_ptr(), bs[2].data_ptr(), Ws[3].data_ptr(), bs[3].data_ptr(),
+            None if kld is None else kld.data_ptr(), mode, scale, ys[j].data_ptr(), None,
+            ws.data_ptr(), need, w.B, w.n, w.n, w.d_model, w.H, code, stream.cuda_stream)
+        assert st == 0, st
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    kern = statistics.mean(per)
+    dk = w.d_model // w.H
+    proj_flops = 4 * 2.0 * w.B * w.n * w.d_model * w.d_model
+    pairs = 0
+    for b in range(w.B):
+        L = w.n if kl is None else int(np.clip(kl[b], 0, w.n))
+        pairs += int(visible_keys(w.n, L, w.causal).sum()) * w.H
+    core_flops = 4.0 * dk * pairs
+    return {
+        "workload": name, "entry": "mha_multihead_forward", "dtype": w.dtype, "B": w.B,
+        "n": w.n, "d_model": w.d_model, "H": w.H, "causal": w.causal,
+        "key_lens": None if w.lens is None else list(w.lens), "input_sets": len(xs),
+        "launches": steps, "layer_ms_mean": kern, "layer_ms_median": statistics.median(per),
+        "layer_ms_min": min(per),
+        "useful_tflops": (proj_flops + core_flops) / (kern * 1e-3) / 1e12,
+        "frac_mfma_peak": (proj_flops + core_flops) / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "projection_flops": proj_flops, "core_useful_flops": core_flops,
+    }
+
+
 def cpu_baseline(w, host, budget_s):
     """The oracle as it stands, on a bounded sample of query rows of the
     headline workload, timed on this host's cores."""
@@ -377,6 +442,10 @@ def main():
         for name in inputs.EXT_ORDER:
             print("bench: %s" % name, file=sys.stderr, flush=True)
             ext.append(bench_ext(torch, mha, name, 100, 20))
+            torch.cuda.empty_cache()
+        for name in inputs.LAYER_ORDER:
+            print("bench: %s" % name, file=sys.stderr, flush=True)
+            ext.append(bench_layer(torch, mha, name, 100, 20))
             torch.cuda.empty_cache()
     traffic = recorded_traffic() if w.name == HEADLINE else None
     cpu = None

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MHA_ABI_VERSION 3
+#define MHA_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum {
@@ -234,6 +234,51 @@ int mha_decode(const void *Q, const void *K, const void *V,
                void *O, float *lse, void *workspace, int64_t workspace_bytes,
                int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
                int64_t d_k, int64_t d_v, int dtype, void *stream);
+
+/*
+ * ---- Multi-head attention with its projections ---------------------------------
+ *
+ * The layer around the core, as the pages write it ("序列建模架构的演进与变革
+ * （二）" §4.9; "Transformer: 详解" §4.2; "第2章：完整的 Transformer 架构"
+ * §2.2):
+ *
+ *     Q = split(Xq Wq^T + bq)    K = split(Xk Wk^T + bk)    V = split(Xv Wv^T + bv)
+ *     O = attention(Q, K, V)     per head, with key_lens and mask_mode as in
+ *                                mha_forward_ex (no ALiBi, H_kv = H)
+ *     Y = concat(O) Wo^T + bo
+ *
+ * split: [B, L, d_model] -> [B, H, L, d_k], d_k = d_model / H; concat is its
+ * inverse.  Self-attention passes the same tensor as Xq, Xk and Xv;
+ * cross-attention passes the decoder states as Xq and the encoder output as
+ * Xk and Xv.
+ *
+ *   Xq        [B, n, d_model]; Xk, Xv [B, m, d_model] (may alias each other)
+ *   W*        [d_model, d_model] in nn.Linear's [out, in] layout, 16-byte aligned
+ *   b*        [d_model] or NULL for no bias
+ *   Y         [B, n, d_model] output
+ *   A         [B, H, n, m] attention weights (as mha_attention_weights), or NULL
+ *   workspace at least mha_multihead_workspace_size bytes, 16-byte aligned,
+ *             overlapping nothing else; it holds Q, K, V and O (and the row
+ *             log-sum-exp when A is requested) during the call.
+ *
+ * All tensors share `dtype`; projections accumulate in fp32 and round
+ * their results (Q, K, V, O, Y) to dtype.  d_k in {64, 128}.  Errors as for
+ * mha_forward_ex, plus MHA_ERR_WORKSPACE; sizes whose tensors pass 2 GiB are
+ * MHA_ERR_UNSUPPORTED.  Enqueues four to five kernels on `stream`.
+ */
+int mha_multihead_workspace_size(int64_t B, int64_t n, int64_t m,
+                                 int64_t d_model, int64_t H, int dtype,
+                                 int need_weights, int64_t *bytes);
+
+int mha_multihead_forward(const void *Xq, const void *Xk, const void *Xv,
+                          const void *Wq, const void *bq, const void *Wk,
+                          const void *bk, const void *Wv, const void *bv,
+                          const void *Wo, const void *bo,
+                          const int32_t *key_lens, int mask_mode, float scale,
+                          void *Y, void *A, void *workspace,
+                          int64_t workspace_bytes, int64_t B, int64_t n,
+                          int64_t m, int64_t d_model, int64_t H, int dtype,
+                          void *stream);
 
 #ifdef __cplusplus
 }

@@ -23,10 +23,11 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"mha_abi_version", "mha_status_string", "mha_validate",
                           "mha_forward", "mha_validate_ex", "mha_forward_ex",
                           "mha_validate_weights", "mha_attention_weights",
-                          "mha_decode_workspace_size", "mha_validate_decode", "mha_decode"}
+                          "mha_decode_workspace_size", "mha_validate_decode", "mha_decode",
+                          "mha_multihead_workspace_size", "mha_multihead_forward"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mha_abi_version() == 3
+    assert lib.mha_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -241,3 +242,43 @@ def test_decode_validation(lib):
     st = lib.mha_decode(Q, K, V, None, None, 0.125, O, None, None, 0, 8, 32, 8, 1, 16384,
                         128, 128, BF16, None)
     assert st == WS
+
+
+# --- multi-head layer --------------------------------------------------------------
+
+def mh_size(B=4, n=128, m=128, dm=512, H=8, dtype=BF16, w=0):
+    import ctypes
+    out = ctypes.c_int64(-1)
+    st = mha.load().mha_multihead_workspace_size(B, n, m, dm, H, dtype, w, ctypes.byref(out))
+    return st, out.value
+
+
+def test_multihead_workspace_size():
+    st, b = mh_size()
+    assert st == OK and b >= 4 * 4 * 128 * 512 * 2
+    assert mh_size(w=1)[1] > b                       # room for the row log-sum-exp
+    assert mh_size(dm=500)[0] == SHAPE               # not a multiple of H
+    assert mh_size(dm=256, H=8)[0] == UNSUP          # d_k = 32
+    assert mh_size(dtype=3)[0] == DTYPE
+
+
+XQ, WQ, WK, WV, WO, Y_, WS_ = (0x100000000 + i * 0x10000000 for i in range(7))
+
+
+def mh_call(lib, ws=WS_, wsb=1 << 27, y=Y_, a=None, mode=0, scale=0.125, B=4, n=128, m=128,
+            dm=512, H=8):
+    return lib.mha_multihead_forward(XQ, XQ, XQ, WQ, None, WK, None, WV, None, WO, None, None,
+                                     mode, scale, y, a, ws, wsb, B, n, m, dm, H, BF16, None)
+
+
+def test_multihead_rejects_on_host(lib):
+    need = mh_size()[1]
+    assert mh_call(lib, wsb=need - 1) == WS
+    assert mh_call(lib, ws=None) == WS
+    assert mh_call(lib, ws=WQ) == WS                 # workspace over a weight
+    assert mh_call(lib, y=XQ) == ALIAS               # output over the input
+    assert mh_call(lib, y=Y_ + 4) == ALIGN
+    assert mh_call(lib, mode=7) == MODE
+    assert mh_call(lib, scale=-1.0) == SCALE
+    assert mh_call(lib, H=5) == SHAPE
+    assert mh_call(lib, B=0) == OK                   # nothing to do

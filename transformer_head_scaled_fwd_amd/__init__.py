@@ -83,6 +83,12 @@ def load():
     lib.mha_decode.argtypes = [vp, vp, vp, vp, vp, fl, vp, vp, vp, i64,
                                i64, i64, i64, i64, i64, i64, i64, i32, vp]
     lib.mha_decode.restype = i32
+    lib.mha_multihead_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32,
+                                                 ctypes.POINTER(i64)]
+    lib.mha_multihead_workspace_size.restype = i32
+    lib.mha_multihead_forward.argtypes = [vp] * 11 + [vp, i32, fl, vp, vp, vp, i64,
+                                                      i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_multihead_forward.restype = i32
     _lib = lib
     return lib
 
@@ -349,6 +355,69 @@ def decode(q, k_cache, v_cache, cache_lens=None, alibi_slopes=None, scale=None,
     return (out, lse) if return_lse else out
 
 
+def multihead_workspace_size(B, n, m, d_model, num_heads, dtype_code, need_weights=False):
+    """Bytes of workspace mha_multihead_forward needs."""
+    out = ctypes.c_int64(0)
+    _check(load().mha_multihead_workspace_size(B, n, m, d_model, num_heads, dtype_code,
+                                               int(bool(need_weights)), ctypes.byref(out)))
+    return int(out.value)
+
+
+def multihead_forward(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, num_heads,
+                      key_lens=None, causal=False, scale=None, need_weights=False,
+                      out=None, workspace=None, stream=None):
+    """Multi-head attention with its projections (mha_multihead_forward).
+
+    xq [B, n, d_model], xk / xv [B, m, d_model]; W* [d_model, d_model] in
+    nn.Linear's [out, in] layout, b* [d_model] or None; scale defaults to
+    1/sqrt(d_model / num_heads).  Returns Y [B, n, d_model], and the
+    weights [B, H, n, m] too when need_weights.
+    """
+    import torch
+    lib = load()
+    code = _dtype_code(xq)
+    dev = xq.device
+    tensors = [xq, xk, xv, Wq, Wk, Wv, Wo] + [b for b in (bq, bk, bv, bo) if b is not None]
+    for t in tensors:
+        if t.dtype != xq.dtype or t.device != dev or not t.is_contiguous():
+            raise ValueError("every tensor must be a contiguous %s tensor on %s" % (xq.dtype, dev))
+    B, n, dm = xq.shape
+    m = xk.shape[1]
+    if tuple(xk.shape) != (B, m, dm) or tuple(xv.shape) != (B, m, dm):
+        raise ValueError("xk and xv must be [B, m, d_model]")
+    for W in (Wq, Wk, Wv, Wo):
+        if tuple(W.shape) != (dm, dm):
+            raise ValueError("weights must be [d_model, d_model]")
+    for b in (bq, bk, bv, bo):
+        if b is not None and tuple(b.shape) != (dm,):
+            raise ValueError("biases must be [d_model]")
+    kl_ptr = None
+    if key_lens is not None:
+        if key_lens.dtype != torch.int32 or key_lens.device != dev or \
+                tuple(key_lens.shape) != (B,):
+            raise ValueError("key_lens must be an int32 tensor [B] on the GPU of xq")
+        kl_ptr = key_lens.data_ptr()
+    H = int(num_heads)
+    if out is None:
+        out = torch.empty((B, n, dm), dtype=xq.dtype, device=dev)
+    A = torch.empty((B, H, n, m), dtype=xq.dtype, device=dev) if need_weights else None
+    need = multihead_workspace_size(B, n, m, dm, H, code, need_weights)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    sc = default_scale(dm // H) if scale is None else float(scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    with torch.cuda.device(dev):
+        st = lib.mha_multihead_forward(
+            ptr(xq), ptr(xk), ptr(xv), ptr(Wq), ptr(bq), ptr(Wk), ptr(bk), ptr(Wv), ptr(bv),
+            ptr(Wo), ptr(bo), kl_ptr, mask_mode(causal), sc, out.data_ptr(), ptr(A),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            B, n, m, dm, H, code, stream)
+    _check(st)
+    return (out, A) if need_weights else out
+
+
 def validate_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=None,
                 out=None, lse=None) -> int:
     """The host-side check of mha_forward_ex only; returns the status."""
@@ -361,7 +430,8 @@ def validate_ex(q, k, v, key_lens=None, causal=False, alibi_slopes=None, scale=N
         ptr(out), ptr(lse), B, H, Hkv, n, m, dk, dv, _dtype_code(q)))
 
 
-__all__ = ["forward", "forward_ex", "attention_weights", "decode", "decode_workspace_size", "validate", "validate_ex",
+__all__ = ["forward", "forward_ex", "attention_weights", "decode", "decode_workspace_size",
+           "multihead_forward", "multihead_workspace_size", "validate", "validate_ex",
            "load", "abi_version", "status_string", "header_functions", "default_scale",
            "mask_mode", "MhaError", "LIB_PATH", "MHA_F32", "MHA_BF16", "MHA_MASK_NONE",
            "MHA_MASK_CAUSAL", "MHA_MASK_CAUSAL_BOTTOM_RIGHT"]

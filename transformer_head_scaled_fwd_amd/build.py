@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmha.so")
 
 SOURCES = ["mha_abi.hip", "mha_fwd_kernel.hip", "mha_weights_kernel.hip",
-           "mha_decode_kernel.hip"]
+           "mha_decode_kernel.hip", "mha_proj_kernel.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [

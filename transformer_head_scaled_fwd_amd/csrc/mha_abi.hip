@@ -283,4 +283,154 @@ int mha_decode(const void* Q, const void* K, const void* V, const int32_t* cache
   return mha::launch_decode(a, p) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
+namespace {
+
+// Workspace of the multi-head forward: Q, K, V, O in [B, H, L, d_k], then
+// the row log-sum-exp when the weights are requested; each part 256-byte
+// aligned.
+struct MhLayout {
+  int64_t q, k, v, o, lse, total;
+};
+
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+MhLayout mh_layout(int64_t B, int64_t n, int64_t m, int64_t d_model, int64_t H, int64_t es,
+                   bool weights) {
+  MhLayout l;
+  l.q = 0;
+  l.k = l.q + round256(B * n * d_model * es);
+  l.v = l.k + round256(B * m * d_model * es);
+  l.o = l.v + round256(B * m * d_model * es);
+  l.lse = l.o + round256(B * n * d_model * es);
+  l.total = l.lse + (weights ? round256(B * H * n * 4) : 0);
+  return l;
+}
+
+int check_multihead_sizes(int64_t B, int64_t n, int64_t m, int64_t d_model, int64_t H,
+                          int dtype) {
+  if (B < 0 || n < 0 || m < 0 || d_model < 0 || H < 0) return MHA_ERR_SHAPE;
+  if (dtype != MHA_F32 && dtype != MHA_BF16) return MHA_ERR_DTYPE;
+  if (H == 0 || d_model % H != 0) return MHA_ERR_SHAPE;
+  const int64_t dk = d_model / H;
+  if (dk != 64 && dk != 128) return MHA_ERR_UNSUPPORTED;
+  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
+  if (B * n * d_model * es >= kMaxHeadBytes || B * m * d_model * es >= kMaxHeadBytes ||
+      d_model * d_model * es >= kMaxHeadBytes)
+    return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+}  // namespace
+
+int mha_multihead_workspace_size(int64_t B, int64_t n, int64_t m, int64_t d_model, int64_t H,
+                                 int dtype, int need_weights, int64_t* bytes) {
+  if (bytes == nullptr) return MHA_ERR_NULL;
+  *bytes = 0;
+  const int st = check_multihead_sizes(B, n, m, d_model, H, dtype);
+  if (st != MHA_OK) return st;
+  *bytes = mh_layout(B, n, m, d_model, H, dtype == MHA_BF16 ? 2 : 4, need_weights != 0).total;
+  return MHA_OK;
+}
+
+int mha_multihead_forward(const void* Xq, const void* Xk, const void* Xv, const void* Wq,
+                          const void* bq, const void* Wk, const void* bk, const void* Wv,
+                          const void* bv, const void* Wo, const void* bo,
+                          const int32_t* key_lens, int mask_mode, float scale, void* Y, void* A,
+                          void* workspace, int64_t workspace_bytes, int64_t B, int64_t n,
+                          int64_t m, int64_t d_model, int64_t H, int dtype, void* stream) {
+  int st = check_multihead_sizes(B, n, m, d_model, H, dtype);
+  if (st != MHA_OK) return st;
+  if (mask_mode < MHA_MASK_NONE || mask_mode > MHA_MASK_CAUSAL_BOTTOM_RIGHT) return MHA_ERR_MODE;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
+  const int64_t es = dtype == MHA_BF16 ? 2 : 4;
+  const int64_t dk = d_model / H;
+  const int64_t xq_b = B * n * d_model * es, xkv_b = B * m * d_model * es;
+  const int64_t w_b = d_model * d_model * es, b_b = d_model * es;
+  const int64_t a_b = A ? B * H * n * m * es : 0;
+  if (B == 0 || n == 0) return MHA_OK;
+  if (Xq == nullptr || Y == nullptr || Wq == nullptr || Wo == nullptr) return MHA_ERR_NULL;
+  if (m > 0 && (Xk == nullptr || Xv == nullptr || Wk == nullptr || Wv == nullptr))
+    return MHA_ERR_NULL;
+  const void* t16[] = {Xq, Xk, Xv, Wq, Wk, Wv, Wo, Y, A, workspace};
+  for (const void* p : t16)
+    if (!aligned16(p)) return MHA_ERR_ALIGN;
+  const void* bias[] = {bq, bk, bv, bo};
+  for (const void* p : bias)
+    if ((uintptr_t)p % es) return MHA_ERR_ALIGN;
+  if (A && n * m * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  // Outputs must not overlap any input or each other.
+  struct R { const void* p; int64_t b; } ins[] = {
+      {Xq, xq_b}, {Xk, xkv_b}, {Xv, xkv_b}, {Wq, w_b}, {Wk, w_b}, {Wv, w_b}, {Wo, w_b},
+      {bq, bq ? b_b : 0}, {bk, bk ? b_b : 0}, {bv, bv ? b_b : 0}, {bo, bo ? b_b : 0},
+      {key_lens, key_lens ? 4 * B : 0}};
+  const MhLayout lay = mh_layout(B, n, m, d_model, H, es, A != nullptr);
+  if (workspace == nullptr || workspace_bytes < lay.total) return MHA_ERR_WORKSPACE;
+  for (const R& r : ins) {
+    if (overlaps(Y, xq_b, r.p, r.b) || overlaps(A, a_b, r.p, r.b)) return MHA_ERR_ALIAS;
+    if (overlaps(workspace, lay.total, r.p, r.b)) return MHA_ERR_WORKSPACE;
+  }
+  if (overlaps(Y, xq_b, A, a_b)) return MHA_ERR_ALIAS;
+  if (overlaps(workspace, lay.total, Y, xq_b) || overlaps(workspace, lay.total, A, a_b))
+    return MHA_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  void* Q = ws + lay.q;
+  void* K = ws + lay.k;
+  void* V = ws + lay.v;
+  void* O = ws + lay.o;
+  float* lse = A ? reinterpret_cast<float*>(ws + lay.lse) : nullptr;
+  const bool bf16 = dtype == MHA_BF16;
+
+  // 1. Q, K, V projections, written head-split.
+  mha::ProjBatch in;
+  const void* xs[3] = {Xq, Xk, Xv};
+  const void* ws_[3] = {Wq, Wk, Wv};
+  const void* bs[3] = {bq, bk, bv};
+  void* outs[3] = {Q, K, V};
+  const int64_t Ls[3] = {n, m, m};
+  for (int j = 0; j < 3; ++j) {
+    mha::ProjProblem& p = in.p[j];
+    p.A = xs[j];
+    p.W = ws_[j];
+    p.bias = bs[j];
+    p.C = outs[j];
+    p.M = (int)(B * Ls[j]);
+    p.N = (int)d_model;
+    p.K = (int)d_model;
+    p.L = (int)(Ls[j] > 0 ? Ls[j] : 1);
+    p.H = (int)H;
+    p.dk = (int)dk;
+    p.a_bytes = B * Ls[j] * d_model * es;
+  }
+  if (mha::launch_proj(in, 3, bf16, false, true, stream) != hipSuccess) return MHA_ERR_HIP;
+  // 2. attention per head (and the row log-sum-exp when weights are asked for).
+  st = launch_forward(Q, K, V, key_lens, mask_mode, nullptr, scale, O, lse, B, H, H, n, m, dk,
+                      dtype, stream);
+  if (st != MHA_OK) return st;
+  // 3. the weights.
+  if (A && m > 0) {
+    st = mha_attention_weights(Q, K, key_lens, mask_mode, nullptr, scale, lse, A, B, H, H, n, m,
+                               dk, dtype, stream);
+    if (st != MHA_OK) return st;
+  }
+  // 4. concatenate the heads and project.
+  mha::ProjBatch out;
+  mha::ProjProblem& p = out.p[0];
+  p.A = O;
+  p.W = Wo;
+  p.bias = bo;
+  p.C = Y;
+  p.M = (int)(B * n);
+  p.N = (int)d_model;
+  p.K = (int)d_model;
+  p.L = (int)n;
+  p.H = (int)H;
+  p.dk = (int)dk;
+  p.a_bytes = B * n * d_model * es;
+  out.p[1] = out.p[0];
+  out.p[2] = out.p[0];
+  return mha::launch_proj(out, 1, bf16, true, false, stream) == hipSuccess ? MHA_OK
+                                                                          : MHA_ERR_HIP;
+}
+
 }  // extern "C"

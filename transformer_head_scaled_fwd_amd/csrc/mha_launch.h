@@ -72,4 +72,22 @@ DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
                        bool bf16);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p);
 
+// One projection C = A W^T + bias: A [M, K] (or, with a_heads, the
+// concatenation of [B, H, L, dk] heads), W [N, K], C [M, N] (or, with
+// c_heads, split into [B, H, L, dk]); M = B * L.
+struct ProjProblem {
+  const void* A;
+  const void* W;
+  const void* bias;  // [N] or nullptr
+  void* C;
+  int M, N, K;
+  int L, H, dk;      // tokens per sequence, heads, head width (head layouts)
+  int64_t a_bytes;   // bytes of A (M * K * element size)
+};
+struct ProjBatch {
+  ProjProblem p[3];
+};
+hipError_t launch_proj(const ProjBatch& b, int count, bool bf16, bool a_heads, bool c_heads,
+                       void* stream);
+
 }  // namespace mha

@@ -189,3 +189,52 @@ def draw_ex(w: ExtWorkload, seed_offset: int = 0):
         key_lens = rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
     return q, k, v, key_lens, (alibi_slopes(w.H) if w.alibi else None)
 
+
+# --- the multi-head layer (projections around the core) --------------------------
+#
+# The pages' base configuration, d_model = 512 with 8 heads of 64
+# ("Transformer: 详解" §4.2; "序列建模架构的演进与变革（二）" §4.9), and their
+# big model's width d_model = 1024 ("Transformer: 详解" §7.2), here with 16
+# heads of 64; sentences padded to the batch maximum, up to 512 tokens.  X ~ N(0, 1); weights and biases ~ U(-1/sqrt(d_model),
+# 1/sqrt(d_model)), nn.Linear's initialisation range, rounded to the dtype.
+
+@dataclass(frozen=True)
+class LayerWorkload:
+    name: str
+    B: int
+    n: int
+    d_model: int
+    H: int
+    dtype: str
+    causal: object
+    lens: Optional[Tuple[int, int]]
+    seed: int
+    note: str = field(default="", compare=False)
+
+
+LAYER_WORKLOADS = {
+    "mha_layer_base_n128": LayerWorkload(
+        "mha_layer_base_n128", B=32, n=128, d_model=512, H=8, dtype="bf16", causal=False,
+        lens=(16, 128), seed=21, note="encoder self-attention layer, base model"),
+    "mha_layer_big_n512": LayerWorkload(
+        "mha_layer_big_n512", B=16, n=512, d_model=1024, H=16, dtype="bf16", causal=True,
+        lens=None, seed=22, note="decoder self-attention layer, big model, 512 tokens"),
+}
+
+LAYER_ORDER = ["mha_layer_base_n128", "mha_layer_big_n512"]
+
+
+def draw_layer(w: LayerWorkload, seed_offset: int = 0):
+    """(x, x, x, [Wq, Wk, Wv, Wo], [bq, bk, bv, bo], key_lens) of a
+    self-attention layer workload, on the CPU."""
+    rng = np.random.Generator(np.random.PCG64(w.seed + seed_offset))
+    x = _round(rng.standard_normal((w.B, w.n, w.d_model)), w.dtype)
+    bound = 1.0 / np.sqrt(w.d_model)
+    Ws = [_round(rng.uniform(-bound, bound, (w.d_model, w.d_model)), w.dtype) for _ in range(4)]
+    bs = [_round(rng.uniform(-bound, bound, w.d_model), w.dtype) for _ in range(4)]
+    key_lens = None
+    if w.lens is not None:
+        lo, hi = w.lens
+        key_lens = rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
+    return x, x, x, Ws, bs, key_lens
+
