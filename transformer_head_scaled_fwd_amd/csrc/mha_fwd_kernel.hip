@@ -154,6 +154,8 @@ struct FwdParams {
   int n, m;           // query rows, key rows per head
   int nqb;            // query blocks per head
   int bottom_right;   // causal alignment: 0 top-left, 1 bottom-right
+  int units_per_xcd;  // K/V heads (batch x H_kv) per XCD, or 0: plain order
+  int unit_group;     // K/V heads one XCD works on at a time
   float scale;        // the caller's scale
   float scale_log2;   // scale * log2(e)
 };
@@ -188,13 +190,33 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   w.hi = w.lane / 32;  // which half of the k / row groups this lane holds
   const int lane = w.lane, li = w.li, hi = w.hi;
 
+  const int n = prm.n, m = prm.m, nqb = prm.nqb;
+  const int bid = blockIdx.x;
+  int qbr, bh;  // query-block rank (0 = first launched) and batch*head
+  if (prm.units_per_xcd > 0) {
+    // Workgroups go to the 8 XCDs round-robin in index order, and each XCD
+    // has its own L2.  Pin every K/V head (a "unit": its group of query heads
+    // times all their query blocks) to one XCD, x = unit % 8, and let the XCD
+    // work through its units unit_group at a time, query-block rank first
+    // within the group, so that the workgroups running together on an XCD
+    // read the same K/V rows.
+    const int x = bid % 8, r = bid / 8;
+    const int per_group = prm.unit_group * prm.group;  // query heads per unit group
+    const int gw = per_group * nqb;                    // workgroups per unit group
+    const int k = r / gw, w_in = r % gw;
+    qbr = w_in / per_group;
+    const int rest = w_in % per_group;
+    const int u = x + 8 * (k * prm.unit_group + rest / prm.group);
+    const int Hkv = prm.H / prm.group;
+    bh = (u / Hkv) * prm.H + (u % Hkv) * prm.group + rest % prm.group;
+  } else {
+    const int BH = gridDim.x / nqb;
+    qbr = bid / BH;
+    bh = bid % BH;
+  }
   // Heaviest query blocks first for causal attention: the work of a block
   // grows with its index, so launching them in reverse evens out the tail.
-  const int n = prm.n, m = prm.m, nqb = prm.nqb;
-  const int BH = gridDim.x / nqb;
-  const int bid = blockIdx.x;
-  const int qb = CAUSAL ? (nqb - 1 - bid / BH) : (bid / BH);
-  const int bh = bid % BH;
+  const int qb = CAUSAL ? (nqb - 1 - qbr) : qbr;
   const int b = bh / prm.H, t = bh % prm.H;
   const int bkv = b * (prm.H / prm.group) + t / prm.group;  // K/V head
   const int q0 = qb * BR;
@@ -344,6 +366,21 @@ static hipError_t launch_one(const LaunchArgs& a) {
   prm.m = (int)a.m;
   prm.nqb = (int)((a.n + BR - 1) / BR);
   prm.bottom_right = a.mode == 2;
+  // XCD pinning of K/V heads (see the kernel) when they split evenly over
+  // the 8 XCDs; unit_group: enough K/V heads per XCD to fill its 32 CUs.
+  const int64_t units = a.B * a.H_kv;
+  prm.units_per_xcd = 0;
+  prm.unit_group = 1;
+  // The plain order already keeps a head's query blocks together on one XCD
+  // when one head's blocks fill it; pinning pays when they do not, or when
+  // several query heads share a K/V head.
+  const int64_t slots = 32 * (NW == 8 ? 1 : 2);  // resident workgroups per XCD
+  const int64_t per_unit = (int64_t)prm.nqb * (a.H / a.H_kv);
+  if (units % 8 == 0 && (a.H != a.H_kv || per_unit < slots)) {
+    prm.units_per_xcd = (int)(units / 8);
+    while ((int64_t)prm.unit_group * per_unit < slots && prm.units_per_xcd % (2 * prm.unit_group) == 0)
+      prm.unit_group *= 2;
+  }
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
