@@ -180,6 +180,40 @@ def time_graph(torch, mha, sets, w, launches=64, replays=5):
     return best
 
 
+def time_copy_floor(torch, nbytes, launches=64, replays=5, rotate_bytes=1 << 30):
+    """GPU-side time per launch of a plain device copy that reads nbytes/2 and
+    writes nbytes/2 (the same HBM bytes as one attention launch), timed like
+    time_graph: `launches` copies over rotating buffers (>= 1 GiB in all, so
+    the last-level cache cannot serve repeats) captured in one HIP graph.
+    It is the floor a launch of this size meets on this device.  Returns
+    microseconds per launch (best replay)."""
+    half = max(1, nbytes // 2)
+    nbuf = max(2, min(64, -(-rotate_bytes // (2 * half))))
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda:0").fill_(i % 251) for i in range(nbuf)]
+    dst = [torch.empty(half, dtype=torch.uint8, device="cuda:0") for _ in range(nbuf)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(launches):
+            dst[i % nbuf].copy_(src[i % nbuf])
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        best = us if best is None else min(best, us)
+    if not torch.equal(dst[0], src[0]):
+        raise RuntimeError("copy floor: graph copy produced wrong bytes")
+    del g, src, dst
+    return best
+
+
 def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     from transformer_head_scaled_fwd_amd import inputs
     w = inputs.WORKLOADS[name]
@@ -199,6 +233,7 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     flops = w.metric_flops()
     useful = 4.0 * w.d * valid_pairs(w, kl)
     abytes = algorithmic_bytes(w, kl)
+    copy_us = time_copy_floor(torch, abytes) if graph_us is not None else None
     avg = total_ms / steps
     kern = statistics.mean(per)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
@@ -219,6 +254,9 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
         "graph_frac_hbm": None if graph_us is None else
         abytes / (graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "graph_tflops": None if graph_us is None else flops / (graph_us * 1e-6) / 1e12,
+        "copy_floor_us": copy_us,
+        "copy_floor_gbps": None if copy_us is None else abytes / (copy_us * 1e-6) / 1e9,
+        "graph_frac_copy_floor": None if copy_us is None else copy_us / graph_us,
     }, host, sets
 
 
@@ -525,6 +563,8 @@ def main():
         "gbps_n128_method": "HIP graph of 64 back-to-back launches over rotating input sets, "
                             "replays checked bit for bit against eager launches; per-launch "
                             "event timing (host launch gaps included) in workloads[].gbps",
+        "copy_floor_gbps_n128": None if sec is None else sec["copy_floor_gbps"],
+        "frac_copy_floor_n128": None if sec is None else sec["graph_frac_copy_floor"],
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                      "kernel": "attn_fwd_kernel<bf16,%d,%s>" % (w.d, "causal" if w.causal else "full"),

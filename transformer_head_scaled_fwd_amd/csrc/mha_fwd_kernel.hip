@@ -220,6 +220,15 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int b = bh / prm.H, t = bh % prm.H;
   const int bkv = b * (prm.H / prm.group) + t / prm.group;  // K/V head
   const int q0 = qb * BR;
+  const int row_w = q0 + wave * kRowsPerWave;
+  const int my_row = row_w + li;
+
+  // Q fragments (MFMA B operand of S^T = K Q^T), kept in registers.  Their
+  // loads go out first: they do not depend on the sequence length, so their
+  // latency overlaps that of the length read the K/V loads wait for.
+  const size_t head_q = (size_t)bh * (size_t)n * D;
+  const auto rq = make_rsrc(Qp + head_q, (uint32_t)n * D * ES);
+  P::issue_q(w.qf, rq, my_row, hi);
 
   int L = m;
   if (key_lens != nullptr) {
@@ -231,8 +240,6 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int off = (CAUSAL && prm.bottom_right) ? L - n : 0;
   const int kend = CAUSAL ? max(0, min(L, q0 + off + BR)) : L;
   const int nkb = (kend + BC - 1) / BC;
-  const int row_w = q0 + wave * kRowsPerWave;
-  const int my_row = row_w + li;
   w.prow_w = row_w + off;
   w.prow = my_row + off;
   // Key blocks any row of this wave can see.
@@ -244,9 +251,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // Buffer resources: out-of-range loads read 0 (also into LDS) and
   // out-of-range stores are dropped, so rows >= n (queries) and >= L (keys,
   // values) need no branch and padded keys are never read from memory.
-  const size_t head_q = (size_t)bh * (size_t)n * D;
   const size_t head_k = (size_t)bkv * (size_t)m * D;
-  const auto rq = make_rsrc(Qp + head_q, (uint32_t)n * D * ES);
   const uint32_t kv_bytes = (uint32_t)L * D * ES;  // rows >= L read as 0
   const auto ro = make_rsrc(Op + head_q, (uint32_t)n * D * ES);
   const T* kbase = Kp + head_k;
@@ -260,15 +265,13 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     G::template stage<false>(lds_v + (j % G::NSTAGE) * G::TILE, vbase, kv_bytes, j, wave, lane);
   };
 
-  // The first key/value blocks are requested before Q so that their memory
-  // latency overlaps the Q loads.
+  // The first key/value blocks, then the wait for Q; the wait before the
+  // first barrier below covers the key/value loads.
   if (nkb > 0) {
     for (int j = 0; j <= DIST && j < nkb; ++j) load_k(j);
     for (int j = 0; j < DIST && j < nkb; ++j) load_v(j);
   }
-
-  // Q fragments (MFMA B operand of S^T = K Q^T), kept in registers.
-  P::load_q(w.qf, rq, my_row, hi);
+  P::pin_q(w.qf);
 
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)

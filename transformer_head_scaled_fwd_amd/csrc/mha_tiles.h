@@ -147,12 +147,20 @@ struct Phase {
   // The loads are completed here: otherwise the in-order memory counter
   // makes every later wait for a prefetch also wait for them.
   MHA_INLINE void load_q(u32x4 (&qf)[NQF], __amdgpu_buffer_rsrc_t rq, int row, int hi) {
+    issue_q(qf, rq, row, hi);
+    pin_q(qf);
+  }
+  // The two halves of load_q, for a caller that issues other loads between
+  // them: the Q loads, then an empty use that makes the compiler wait for them.
+  MHA_INLINE void issue_q(u32x4 (&qf)[NQF], __amdgpu_buffer_rsrc_t rq, int row, int hi) {
     constexpr int ES = (int)sizeof(T);
 #pragma unroll
     for (int s = 0; s < NQF; ++s) {
       const uint32_t col = BF16 ? (16 * s + 8 * hi) : (4 * s + (D / 2) * hi);
       qf[s] = load16(rq, ((uint32_t)row * D + col) * ES);
     }
+  }
+  MHA_INLINE void pin_q(const u32x4 (&qf)[NQF]) {
 #pragma unroll
     for (int s = 0; s < NQF; ++s) asm volatile("" : : "v"(qf[s]));
   }
