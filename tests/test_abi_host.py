@@ -73,6 +73,36 @@ def test_each_error_status(lib, kw, status):
     assert val(lib, **kw) == status
 
 
+# Far-apart fake addresses for tensors near the size limits.
+BIG = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40)
+
+
+def test_size_limits(lib):
+    # A head's tensor must stay under 2 GiB (32-bit buffer offsets): for
+    # bf16 rows of 128 elements that is n, m <= 2^23 - 1.
+    lim = (1 << 23) - 1
+    assert val(lib, n=lim, m=64, dk=128, dv=128, **BIG) == OK
+    assert val(lib, n=lim + 1, m=64, dk=128, dv=128, **BIG) == UNSUP
+    assert val(lib, n=64, m=lim, dk=128, dv=128, **BIG) == OK
+    assert val(lib, n=64, m=lim + 1, dk=128, dv=128, **BIG) == UNSUP
+    assert val(lib, n=(1 << 22) - 1, m=64, dk=128, dv=128, dtype=F32, **BIG) == OK
+    assert val(lib, n=1 << 22, m=64, dk=128, dv=128, dtype=F32, **BIG) == UNSUP
+
+
+def test_grid_limit(lib):
+    # The dispatch grid counts work-items in 32 bits: 256 per 128 query rows.
+    full = (1 << 32) // 256          # workgroups that would reach 2^32 work-items
+    assert val(lib, B=full // 256 - 1, H=256, n=128, m=16, **BIG) == OK
+    assert val(lib, B=full // 256, H=256, n=128, m=16, **BIG) == UNSUP
+    assert val(lib, B=1, H=1, n=(1 << 22) - 1, m=16, dk=64, dv=64, **BIG) == OK
+
+
+def test_huge_sizes_are_rejected_not_wrapped(lib):
+    for kw in (dict(n=1 << 62), dict(m=1 << 62), dict(B=1 << 40), dict(H=1 << 40),
+               dict(B=1 << 31, H=1 << 31)):
+        assert val(lib, **dict(BIG, **kw)) == UNSUP, kw
+
+
 def test_q_k_v_may_alias_each_other(lib):
     assert val(lib, k=Q, v=Q) == OK
 

@@ -115,6 +115,57 @@ def test_ragged_shapes(gpu, B, H, n, m, d, dt, causal, lens):
         assert torch.count_nonzero(o[0]) == 0
 
 
+# --- the largest heads the C ABI accepts -------------------------------------------
+# A head's tensor must stay under 2 GiB (the kernels address a head with
+# 32-bit buffer offsets): for bf16 rows of d = 128 that is n, m <= 2^23 - 1.
+
+def test_max_query_rows_per_head(gpu):
+    n, m, d = (1 << 23) - 1, 100, 128
+    _say("max query rows: n=%d m=%d d=%d bf16 (Q and O heads of %.4f GiB)"
+         % (n, m, d, n * d * 2 / 2 ** 30))
+    dev = "cuda:0"
+    q = inputs.device_normal((1, 1, n, d), seed=31)
+    _, k, v, _ = inputs.draw(1, 1, 1, m, d, d, "bf16", seed=32)
+    o = mha.forward(q, k.to(dev), v.to(dev))
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(33))
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(n - 200, n),
+                                     rng.integers(0, n, 200)]))
+    idx = torch.as_tensor(rows, device=dev)
+    qs = q[0, 0].index_select(0, idx).cpu().reshape(1, 1, len(rows), d)
+    got = o[0, 0].index_select(0, idx).cpu().reshape(1, 1, len(rows), d)
+    ref = oracle.attention(qs, k, v)
+    compare(got, ref, TOL["bf16"], "max n, %d sampled rows" % len(rows))
+    del q, o
+    torch.cuda.empty_cache()
+
+
+def test_max_key_rows_per_head(gpu):
+    # Q = 0 makes every valid score equal, so each output row is the mean of
+    # the valid value rows ("序列建模架构的演进与变革（二）" §4.3: weights sum to
+    # 1).  Rows past the length hold NaN and must never be read.
+    n, m, d = 64, (1 << 23) - 1, 128
+    L = m - 7
+    _say("max key rows: n=%d m=%d (valid %d) d=%d bf16" % (n, m, L, d))
+    dev = "cuda:0"
+    k = inputs.device_normal((1, 1, m, d), seed=34)
+    v = inputs.device_normal((1, 1, m, d), seed=35)
+    k[0, 0, L:] = float("nan")
+    v[0, 0, L:] = float("nan")
+    q = torch.zeros((1, 1, n, d), dtype=torch.bfloat16, device=dev)
+    kl = torch.tensor([L], dtype=torch.int32, device=dev)
+    o = mha.forward(q, k, v, key_lens=kl)
+    torch.cuda.synchronize()
+    vh = v[0, 0, :L].cpu()
+    total = np.zeros(d)
+    for c0 in range(0, L, 1 << 20):
+        total += oracle.to_f64(vh[c0:c0 + (1 << 20)]).sum(axis=0)
+    ref = np.broadcast_to(total / L, (1, 1, n, d))
+    compare(o.cpu(), ref, TOL["bf16"], "max m, Q = 0")
+    del k, v, o
+    torch.cuda.empty_cache()
+
+
 # --- the pages' worked examples on the GPU -----------------------------------------
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

@@ -23,6 +23,23 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // head with 32-bit buffer offsets.
 constexpr int64_t kMaxHeadBytes = (int64_t)1 << 31;
 
+// a * b for non-negative sizes, saturating at INT64_MAX instead of wrapping.
+int64_t mul_sat(int64_t a, int64_t b) {
+  if (a == 0 || b == 0) return 0;
+  return a > INT64_MAX / b ? INT64_MAX : a * b;
+}
+
+// Whether `count` elements of `bytes_each` bytes stay under kMaxHeadBytes.
+bool head_fits(int64_t count, int64_t bytes_each) {
+  return count <= (kMaxHeadBytes - 1) / bytes_each;
+}
+
+// A dispatch counts its grid in work-items, in 32 bits: `blocks` workgroups
+// of `threads` work-items each must stay within that.
+bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= (int64_t)UINT32_MAX / threads;
+}
+
 // Shared checks of the forward entry points.  H_kv: K/V heads; mode 0/1/2.
 int check_forward(const void* Q, const void* K, const void* V, const int32_t* key_lens, int mode,
                   const float* alibi, float scale, const void* O, const float* lse, int64_t B,
@@ -35,10 +52,11 @@ int check_forward(const void* Q, const void* K, const void* V, const int32_t* ke
   if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
   if (d_k != d_v || (d_k != 64 && d_k != 128)) return MHA_ERR_UNSUPPORTED;
   const int64_t es = dtype == MHA_BF16 ? 2 : 4;
-  if (n * d_k * es >= kMaxHeadBytes || m * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
-  const int64_t rows_per_block = 128;
-  const int64_t blocks = ((n + rows_per_block - 1) / rows_per_block) * B * H;
-  if (B > INT32_MAX || H > INT32_MAX || blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  if (!head_fits(n, d_k * es) || !head_fits(m, d_k * es)) return MHA_ERR_UNSUPPORTED;
+  // Grid: workgroups of 4 waves over 128 query rows (the launcher takes 8
+  // waves over 256 rows only where that grid fits as well).
+  if (B > INT32_MAX || H > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  if (!grid_fits(mul_sat(mul_sat((n + 127) / 128, B), H), 256)) return MHA_ERR_UNSUPPORTED;
   const int64_t q_bytes = B * H * n * d_k * es;
   const int64_t kv_bytes = B * H_kv * m * d_k * es;
   const int64_t o_bytes = B * H * n * d_v * es;
@@ -160,10 +178,10 @@ int mha_validate_weights(const void* Q, const void* K, const int32_t* key_lens, 
   if (!std::isfinite(scale) || !(scale > 0.0f)) return MHA_ERR_SCALE;
   if (d_k != 64 && d_k != 128) return MHA_ERR_UNSUPPORTED;
   const int64_t es = dtype == MHA_BF16 ? 2 : 4;
-  if (n * d_k * es >= kMaxHeadBytes || m * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
-  if (n > 0 && m > 0 && n * m * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
-  const int64_t blocks = ((n + 127) / 128) * B * H;
-  if (B > INT32_MAX || H > INT32_MAX || blocks > INT32_MAX) return MHA_ERR_UNSUPPORTED;
+  if (!head_fits(n, d_k * es) || !head_fits(m, d_k * es)) return MHA_ERR_UNSUPPORTED;
+  if (n > 0 && m > 0 && !head_fits(mul_sat(n, m), es)) return MHA_ERR_UNSUPPORTED;
+  if (B > INT32_MAX || H > INT32_MAX || !grid_fits(mul_sat(mul_sat((n + 127) / 128, B), H), 256))
+    return MHA_ERR_UNSUPPORTED;
   const int64_t q_bytes = B * H * n * d_k * es;
   const int64_t k_bytes = B * H_kv * m * d_k * es;
   const int64_t a_bytes = B * H * n * m * es;
@@ -231,10 +249,14 @@ int mha_validate_decode(const void* Q, const void* K, const void* V, const int32
                          O, lse, B, H, H_kv, n, m, d_k, d_v, dtype);
   if (st != MHA_OK) return st;
   const int64_t es = dtype == MHA_BF16 ? 2 : 4;
-  if (H * n * d_k * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  if (!head_fits(mul_sat(H, n), d_k * es)) return MHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || n == 0) return MHA_OK;
   const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
-  if (B * H_kv * p.nrs * p.nsplit > INT32_MAX || B * H * n > INT32_MAX)
+  // Grids: the decode kernel (at most 4 waves per workgroup) and the merge
+  // of the splits (4 rows per 256 work-items).
+  const int64_t rows = mul_sat(mul_sat(B, H), n);
+  if (rows > INT32_MAX || !grid_fits(mul_sat(mul_sat(mul_sat(B, H_kv), p.nrs), p.nsplit), 256) ||
+      !grid_fits((rows + 3) / 4, 256))
     return MHA_ERR_UNSUPPORTED;
   if (p.workspace_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.workspace_bytes || !aligned16(workspace))
@@ -314,8 +336,8 @@ int check_multihead_sizes(int64_t B, int64_t n, int64_t m, int64_t d_model, int6
   const int64_t dk = d_model / H;
   if (dk != 64 && dk != 128) return MHA_ERR_UNSUPPORTED;
   const int64_t es = dtype == MHA_BF16 ? 2 : 4;
-  if (B * n * d_model * es >= kMaxHeadBytes || B * m * d_model * es >= kMaxHeadBytes ||
-      d_model * d_model * es >= kMaxHeadBytes)
+  if (!head_fits(mul_sat(mul_sat(B, n), d_model), es) ||
+      !head_fits(mul_sat(mul_sat(B, m), d_model), es) || !head_fits(mul_sat(d_model, d_model), es))
     return MHA_ERR_UNSUPPORTED;
   return MHA_OK;
 }
@@ -357,7 +379,7 @@ int mha_multihead_forward(const void* Xq, const void* Xk, const void* Xv, const 
   const void* bias[] = {bq, bk, bv, bo};
   for (const void* p : bias)
     if ((uintptr_t)p % es) return MHA_ERR_ALIGN;
-  if (A && n * m * es >= kMaxHeadBytes) return MHA_ERR_UNSUPPORTED;
+  if (A && !head_fits(mul_sat(n, m), es)) return MHA_ERR_UNSUPPORTED;
   // Outputs must not overlap any input or each other.
   struct R { const void* p; int64_t b; } ins[] = {
       {Xq, xq_b}, {Xk, xkv_b}, {Xv, xkv_b}, {Wq, w_b}, {Wk, w_b}, {Wv, w_b}, {Wo, w_b},

@@ -408,7 +408,8 @@ template <typename T, int D>
 static hipError_t launch_d(const LaunchArgs& a) {
   if constexpr (D == 128 && sizeof(T) == 2) {
     const int64_t big_blocks = ((a.n + 255) / 256) * a.B * a.H;
-    if (big_blocks >= 4 * 256) return launch_variant<T, D, 8>(a);
+    if (big_blocks >= 4 * 256 && big_blocks <= (int64_t)UINT32_MAX / 512)
+      return launch_variant<T, D, 8>(a);
   }
   return launch_variant<T, D, 4>(a);
 }

@@ -238,3 +238,16 @@ def draw_layer(w: LayerWorkload, seed_offset: int = 0):
         key_lens = rng.integers(lo, hi + 1, size=w.B).astype(np.int32)
     return x, x, x, Ws, bs, key_lens
 
+
+
+def device_normal(shape, seed: int, dtype: str = "bf16", device: str = "cuda:0") -> torch.Tensor:
+    """N(0, 1) values drawn on the device, for tensors too large to draw and
+    copy from the host (heads near the 2 GiB limit): torch's seeded device
+    generator in float32, then rounded to the storage dtype with
+    round-to-nearest-even.  Callers that check such a tensor against the
+    oracle copy the rows they sample back to the host, so both sides still
+    see the same bits."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x if dtype == "f32" else x.to(torch.bfloat16)
