@@ -222,29 +222,61 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   }
 }
 
-// Merge of the splits: one wave per query row, lanes over the features.
+// Merge of the splits: one wave per query row.  Lane s holds split s's
+// running max and row sum (64 splits at a time), so the row's max M and the
+// weighted sum come from one round of loads and two wave reductions; the
+// unnormalised outputs are then summed with the lanes over the features,
+// eight splits' loads in flight at a time.
 template <typename T, int D>
 __global__ void __launch_bounds__(256)
 attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                            T* __restrict__ Op, float* __restrict__ lse, int rows, int nsplit) {
-  const int row = blockIdx.x * 4 + threadIdx.x / 64;
+  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / 64);
   const int lane = threadIdx.x % 64;
   if (row >= rows) return;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
+  const float* po = part_o + (size_t)row * nsplit * D;
   float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
   float lsum = 0.0f;
   float acc[D / 64];
 #pragma unroll
   for (int u = 0; u < D / 64; ++u) acc[u] = 0.0f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float ms = ml[2 * s];
-    const float f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-    lsum += f * ml[2 * s + 1];
-    const float* po = part_o + ((size_t)row * nsplit + s) * D;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    // This lane's split: its weight 2^(m_s - M) (0 for a split with no key).
+    float f = 0.0f;
+    if (s0 + lane < nsplit) {
+      const float ms = ml[2 * (s0 + lane)];
+      f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      lsum += f * ml[2 * (s0 + lane) + 1];
+    }
+    const int cnt = min(64, nsplit - s0);
+    int j = 0;
+    for (; j + 8 <= cnt; j += 8) {
+      float v[8][D / 64];
 #pragma unroll
-    for (int u = 0; u < D / 64; ++u) acc[u] += f * po[lane + 64 * u];
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) v[q][u] = po[(size_t)(s0 + j + q) * D + lane + 64 * u];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float fq = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j + q));
+#pragma unroll
+        for (int u = 0; u < D / 64; ++u) acc[u] += fq * v[q][u];
+      }
+    }
+    for (; j < cnt; ++j) {
+      const float fq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+      for (int u = 0; u < D / 64; ++u) acc[u] += fq * po[(size_t)(s0 + j) * D + lane + 64 * u];
+    }
   }
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) lsum += __shfl_xor(lsum, x);
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int u = 0; u < D / 64; ++u) Op[(size_t)row * D + lane + 64 * u] = (T)(acc[u] * inv);
@@ -267,9 +299,13 @@ DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
   p.nrs = (R + kRowsPerWave - 1) / kRowsPerWave;
   const int64_t nkb = (m + BC - 1) / BC;
   const int64_t units = B * H_kv * p.nrs;
-  // About four workgroups per CU of a 256-CU device, with at least one key
-  // block per wave in every split.
-  const int64_t target = 1024;
+  // About one workgroup per CU of a 256-CU device (a workgroup's four K/V
+  // tile pairs take 128 KiB of the CU's 160 KiB of LDS, so one is resident at
+  // a time): each wave then streams several key blocks, the next block's
+  // loads overlapping the current block's compute, instead of one block per
+  // wave and several rounds of workgroups.  At least one key block per wave
+  // in every split.
+  const int64_t target = 256;
   int64_t nsplit = units >= target ? 1 : (target + units - 1) / units;
   const int64_t max_split = (nkb + nw - 1) / nw;
   if (nsplit > max_split) nsplit = max_split;
