@@ -108,3 +108,29 @@ def test_decode_workload_every_row(gpu, name):
                                          alibi_slopes=sl, scale=w.scale)
     assert maxerr(o.reshape(-1, w.d), ref, "O") <= TOL_O[w.dtype]
     assert maxerr(lse.reshape(-1), lref, "lse") <= TOL_LSE[w.dtype]
+
+
+def test_decode_at_the_per_head_limit(gpu):
+    # A cache head of 2^23 - 1 rows of d = 128 bf16, just under the 2 GiB the
+    # kernels' 32-bit offsets allow, filled to L rows; NaN past L.  With
+    # Q = 0 every visible score is equal, so the output is the mean of the
+    # valid value rows ("序列建模架构的演进与变革（二）" §4.3: the weights sum
+    # to 1), whatever the split of the key axis.
+    m, d = (1 << 23) - 1, 128
+    L = m - 5
+    _say("decode at the limit: m=%d (filled %d) d=%d bf16" % (m, L, d))
+    k = inputs.device_normal((1, 1, m, d), seed=44)
+    v = inputs.device_normal((1, 1, m, d), seed=45)
+    k[0, 0, L:] = float("nan")
+    v[0, 0, L:] = float("nan")
+    q = torch.zeros((1, 1, 1, d), dtype=torch.bfloat16, device=DEV)
+    o = mha.decode(q, k, v, cache_lens=torch.tensor([L], dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    vh = v[0, 0, :L].cpu()
+    total = np.zeros(d)
+    for c0 in range(0, L, 1 << 20):
+        total += oracle.to_f64(vh[c0:c0 + (1 << 20)]).sum(axis=0)
+    ref = (total / L).reshape(1, 1, 1, d)
+    assert maxerr(o.cpu(), ref, "O") <= TOL_O["bf16"]
+    del k, v, o
+    torch.cuda.empty_cache()

@@ -219,3 +219,36 @@ def test_weights_workload_full(gpu):
     assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[w.dtype]
     assert maxerr(a, a_ref, "A") <= TOL_A[w.dtype]
     assert np.all(oracle.to_f64(a)[a_ref == 0.0] == 0.0)
+
+
+def test_weights_at_the_per_head_limit(gpu):
+    # A head of the weights is n x m elements and must stay under 2 GiB (the
+    # kernels' 32-bit offsets): n = m = 32767 bf16 is 2,147,352,578 bytes.
+    # Sampled rows, among them the last, against the oracle on those rows.
+    n = m = 32767
+    d = 64
+    L = m - 3
+    _say("weights at the limit: n=m=%d d=%d bf16, L=%d (%.4f GiB per head)"
+         % (n, d, L, n * m * 2 / 2 ** 30))
+    q, k, v, _ = inputs.draw(1, 1, n, m, d, d, "bf16", seed=41)
+    kl = np.array([L], np.int32)
+    o, lse, a = mha.forward_ex(q.to(DEV), k.to(DEV), v.to(DEV),
+                               key_lens=torch.as_tensor(kl).to(DEV),
+                               return_lse=True, need_weights=True)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(42))
+    rows = np.unique(np.concatenate([[0, 1, 31, 32], np.arange(n - 40, n),
+                                     rng.integers(0, n, 20)]))
+    idx = torch.as_tensor(rows, device=DEV)
+    a_s = a[0, 0].index_select(0, idx).cpu().reshape(1, 1, len(rows), m)
+    o_s = o[0, 0].index_select(0, idx).cpu().reshape(1, 1, len(rows), d)
+    qs = q[0, 0][torch.as_tensor(rows)].reshape(1, 1, len(rows), d)
+    o_ref, _, _, a_ref = oracle.attention_ex(qs, k, v, key_lens=kl, scale=mha.default_scale(d),
+                                             return_lse=True, return_weights=True)
+    assert maxerr(o_s, o_ref, "O") <= TOL_O["bf16"]
+    assert maxerr(a_s, a_ref, "A") <= TOL_A["bf16"]
+    a64 = oracle.to_f64(a_s)
+    assert np.all(a64[..., L:] == 0.0)
+    assert np.all(np.isfinite(a64))
+    del o, lse, a
+    torch.cuda.empty_cache()
