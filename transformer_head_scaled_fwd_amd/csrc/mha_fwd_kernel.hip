@@ -160,8 +160,15 @@ struct FwdParams {
   float scale_log2;   // scale * log2(e)
 };
 
+// Resident workgroups per CU: one for 8 waves, or when the fp32 d = 128
+// tiles take 128 KiB of LDS; otherwise two.
+template <typename T, int D, int NW>
+constexpr int fwd_wg_per_cu() {
+  return (NW == 8 || (sizeof(T) == 4 && D == 128)) ? 1 : 2;
+}
+
 template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
-__global__ void __launch_bounds__(64 * NW, 2)
+__global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<T, D, NW>()))
 attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
                 const T* __restrict__ Vp, const int32_t* __restrict__ key_lens,
                 const float* __restrict__ alibi_slopes, T* __restrict__ Op,
@@ -377,7 +384,7 @@ static hipError_t launch_one(const LaunchArgs& a) {
   // The plain order already keeps a head's query blocks together on one XCD
   // when one head's blocks fill it; pinning pays when they do not, or when
   // several query heads share a K/V head.
-  const int64_t slots = 32 * (NW == 8 ? 1 : 2);  // resident workgroups per XCD
+  const int64_t slots = 32 * fwd_wg_per_cu<T, D, NW>();  // resident workgroups per XCD
   const int64_t per_unit = (int64_t)prm.nqb * (a.H / a.H_kv);
   if (units % 8 == 0 && (a.H != a.H_kv || per_unit < slots)) {
     prm.units_per_xcd = (int)(units / 8);
