@@ -12,7 +12,10 @@ kernel, the other workloads (GB/s and TFLOP/s each against its roofline,
 inputs rotated over >= 1 GiB so the 256 MB last-level cache cannot serve
 repeats), the workloads of the extended entry points (grouped K/V heads,
 ALiBi, the weights output), and the CPU oracle timed on a bounded sample of
-the headline workload on this host's cores.
+the headline workload on this host's cores.  The same leg compares the
+oracle with each workload's GPU output on the same input bits (every output
+of the smaller workloads, the sampled rows of the headline) and reports the
+max-abs error, the bf16 store floor and the oracle's time.
 """
 from __future__ import annotations
 
@@ -133,7 +136,7 @@ def time_launches(torch, mha, sets, w, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
-    return t0.elapsed_time(t1), per
+    return t0.elapsed_time(t1), per, outs[0]
 
 
 def time_graph(torch, mha, sets, w, launches=64, replays=5):
@@ -227,7 +230,8 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     for s in range(1, nsets):
         q, k, v = (torch.roll(t, shifts=s, dims=0).contiguous() + 0 for t in first[:3])
         sets.append((q, k, v, first[3], first[4]))
-    total_ms, per = time_launches(torch, mha, sets, w, steps, warmup)
+    total_ms, per, out0 = time_launches(torch, mha, sets, w, steps, warmup)
+    out0 = out0.cpu()  # the output of the first input set, the host inputs
     graph_us = time_graph(torch, mha, sets, w) if w.metric_flops() < 1e11 else None
     kl = first[4]
     flops = w.metric_flops()
@@ -257,7 +261,7 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
         "copy_floor_us": copy_us,
         "copy_floor_gbps": None if copy_us is None else abytes / (copy_us * 1e-6) / 1e9,
         "graph_frac_copy_floor": None if copy_us is None else copy_us / graph_us,
-    }, host, sets
+    }, host, sets, out0
 
 
 def visible_keys(n, L, causal):
@@ -464,14 +468,58 @@ def cpu_baseline(w, host, budget_s):
     target = max(64, int(len(probe) * budget_s / dt))
     rows = sample(min(target, 200000))
     t = time.perf_counter()
-    oracle.attention_rows(Q, K, V, rows, key_lens=kl, causal=w.causal, scale=w.scale)
+    ref = oracle.attention_rows(Q, K, V, rows, key_lens=kl, causal=w.causal, scale=w.scale)
     dt = time.perf_counter() - t
     f = work(rows)
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle", "seconds": dt, "probe_rate_tflops": rate / 1e12,
             "sample": "%d query rows drawn uniformly (seeded) from the %d heads of %s; "
                       "useful FLOPs 4*d*(valid keys) per row; fp64 on the host cores"
-                      % (len(rows), w.B * w.H, w.name)}
+                      % (len(rows), w.B * w.H, w.name)}, rows, ref, dt
+
+
+TOL = {"f32": 1e-5, "bf16": 1.5e-2}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def parity(w, host, out, rows=None, ref=None, oracle_s=None):
+    """The oracle (timed on this host's cores) against the GPU output of the
+    same input bits: max-abs error over every element, or over the sampled
+    rows when `rows` is given (with the oracle's result `ref` for them)."""
+    import oracle
+    q, k, v, kl = host
+    if ref is None:
+        t = time.perf_counter()
+        ref = oracle.attention(q, k, v, key_lens=kl, causal=w.causal, scale=w.scale)
+        oracle_s = time.perf_counter() - t
+        got = oracle.to_f64(out)
+        compared = "all %d outputs" % got.size
+    else:
+        import torch
+        r = torch.from_numpy(rows)
+        got = oracle.to_f64(out[r[:, 0], r[:, 1], r[:, 2]])
+        compared = "%d sampled rows" % len(rows)
+    err = np.abs(got - ref)
+    floor = None
+    if w.dtype == "bf16":
+        import torch
+        r32 = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float32))
+        floor = float(np.abs(r32.to(torch.bfloat16).double().numpy() - ref).max())
+    mx = float(err.max()) if err.size else 0.0
+    return {"compared": compared, "max_abs_err": mx,
+            "mean_abs_err": float(err.mean()) if err.size else 0.0,
+            "store_floor": floor, "tol": TOL[w.dtype], "pass": bool(mx <= TOL[w.dtype]),
+            "oracle_s": oracle_s, "oracle_threads": oracle.threads(), "cpu_model": cpu_model()}
 
 
 def calibrate_copy(torch, nbytes):
@@ -514,16 +562,18 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     print("bench: %s steps=%d warmup=%d" % (w.name, args.steps, args.warmup),
           file=sys.stderr, flush=True)
-    head, host, _ = bench_workload(torch, mha, w.name, args.steps, args.warmup)
+    head, host, _, head_out = bench_workload(torch, mha, w.name, args.steps, args.warmup)
     others = []
+    checks = []  # (workload, host inputs, GPU output) for the oracle comparison
     if not args.no_others:
         for name in inputs.ORDER:
             if name == w.name:
                 continue
             print("bench: %s" % name, file=sys.stderr, flush=True)
-            res, _, sets = bench_workload(torch, mha, name, 200, 20)
+            res, o_host, sets, o_out = bench_workload(torch, mha, name, 200, 20)
             del sets
             others.append(res)
+            checks.append((inputs.WORKLOADS[name], o_host, o_out, res))
             torch.cuda.empty_cache()
     ext = []
     if not args.no_others:
@@ -539,7 +589,11 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, host, args.cpu_seconds)
+        cpu, rows, ref, dt = cpu_baseline(w, host, args.cpu_seconds)
+        head["parity"] = parity(w, host, head_out, rows=rows, ref=ref, oracle_s=dt)
+        for wk, o_host, o_out, res in checks:
+            print("bench: oracle parity %s" % wk.name, file=sys.stderr, flush=True)
+            res["parity"] = parity(wk, o_host, o_out)
     bf16 = w.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_MFMA_TFLOPS
     kern_s = head["kernel_ms_mean"] * 1e-3
@@ -573,6 +627,8 @@ def main():
                      "kernel_source_sha256_16": kernel_source_hash(),
                      "flops_per_launch": head["metric_flops"]},
         "cpu_baseline": cpu,
+        "parity_all_pass": None if cpu is None else
+        all(r["parity"]["pass"] for r in [head] + others if "parity" in r),
         "workloads": [head] + others,
         "extended": ext,
         "device": device_info(torch),
