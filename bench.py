@@ -516,7 +516,10 @@ def parity(w, host, out, rows=None, ref=None, oracle_s=None):
         r32 = torch.from_numpy(np.ascontiguousarray(ref, dtype=np.float32))
         floor = float(np.abs(r32.to(torch.bfloat16).double().numpy() - ref).max())
     mx = float(err.max()) if err.size else 0.0
-    return {"compared": compared, "max_abs_err": mx,
+    at = [int(x) for x in np.unravel_index(np.argmax(err), err.shape)] if err.size else []
+    if rows is not None and at:
+        at = [int(x) for x in rows[at[0]]] + at[1:]  # (b, head, row, column)
+    return {"compared": compared, "max_abs_err": mx, "max_at": at,
             "mean_abs_err": float(err.mean()) if err.size else 0.0,
             "store_floor": floor, "tol": TOL[w.dtype], "pass": bool(mx <= TOL[w.dtype]),
             "oracle_s": oracle_s, "oracle_threads": oracle.threads(), "cpu_model": cpu_model()}

@@ -85,6 +85,25 @@ def test_workload_long_causal_sampled_rows(gpu):
     assert torch.isfinite(o.float()).all()
 
 
+def test_workload_long_causal_every_element(gpu):
+    """Every element of the long causal workload against the oracle, one head
+    at a time (the oracle's row mode over all n rows of the head)."""
+    w = inputs.WORKLOADS["causal_n16384_d128"]
+    _say("workload %s (every element)" % w.name)
+    q, k, v, kl = inputs.make(w)
+    o = run_gpu(q, k, v, kl, w.causal, w.scale)
+    worst = 0.0
+    floor = 0.0
+    for t in range(w.H):
+        rows = np.stack([np.zeros(w.n, np.int64), np.full(w.n, t, np.int64),
+                         np.arange(w.n, dtype=np.int64)], 1)
+        ref = oracle.attention_rows(q, k, v, rows, key_lens=kl, causal=True, scale=w.scale)
+        floor = max(floor, store_floor(ref))
+        worst = max(worst, compare(o[0, t], ref, TOL["bf16"], "%s head %d" % (w.name, t)))
+    _say("%s: max_abs_err %.3e over all %d outputs, store floor %.3e"
+         % (w.name, worst, o.numel(), floor))
+
+
 # --- shapes spanning several tiles with ragged tails ------------------------------
 
 CASES = [
