@@ -22,7 +22,12 @@
 // attention kernel, the tile is computed transposed (W rows on the MFMA M
 // axis), so each lane ends up holding one output row and four consecutive
 // output columns, stored as one 8- or 16-byte write.  Up to three problems
-// (Q, K and V projections) share one launch.
+// (Q, K and V projections) share one launch, one grid row each.
+//
+// Tile order: workgroups go to the 8 XCDs round-robin in index order and
+// each XCD has its own L2, so XCD x is given a contiguous band of tile rows
+// with all their column tiles.  A row band is then read by one XCD only,
+// and the workgroups running together on it share A and W tiles in L2.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -58,8 +63,11 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
 
   const ProjProblem pb = blockIdx.y == 0 ? batch.p[0] : (blockIdx.y == 1 ? batch.p[1] : batch.p[2]);
   const int tiles_m = (pb.M + BM - 1) / BM, tiles_n = (pb.N + BN - 1) / BN;
-  if ((int)blockIdx.x >= tiles_m * tiles_n) return;  // the whole workgroup leaves
-  const int tn = blockIdx.x % tiles_n, tm = blockIdx.x / tiles_n;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if (t >= total) return;  // the whole workgroup leaves
+  if (total % 8 == 0) t = (t % 8) * (total / 8) + t / 8;
+  const int tn = t % tiles_n, tm = t / tiles_n;
   const int row0 = tm * BM, col0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -129,15 +137,13 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
       for (int e = 0; e < 16; ++e) acc[jn][im][e] = 0.0f;
 
   const int nkt = K / BK;
+  // Two stages: step kt's barrier, after the wait for its own tile, also
+  // retires every read of step kt-1, whose slot then receives step kt+1.
   load(0, 0);
   for (int kt = 0; kt < nkt; ++kt) {
-    if (kt + 1 < nkt) {
-      load(kt + 1, (kt + 1) & 1);
-      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * LOADS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (kt + 1 < nkt) load(kt + 1, (kt + 1) & 1);
     const char* ta = smem + (kt & 1) * 2 * TILE;
     const char* tw = ta + TILE;
     if constexpr (BF16) {
@@ -181,7 +187,6 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
                                                                   acc[jn][im], 0, 0, 0);
       }
     }
-    __syncthreads();  // the stage is read before it is refilled
   }
 
   // Epilogue: lane holds output row row0 + 64wr + 32im + li and columns
