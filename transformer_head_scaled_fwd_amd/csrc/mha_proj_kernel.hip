@@ -136,6 +136,29 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[jn][im][e] = 0.0f;
 
+  // Bias of this lane's 32 output columns (see the epilogue), requested
+  // before the K loop so that its latency hides behind the first tile's:
+  // element loads through a buffer resource, so no bias (0 records) and
+  // columns past N read 0 without a branch.
+  float bv[2][4][4];
+  {
+    const auto rb = make_rsrc(pb.bias, pb.bias != nullptr ? (uint32_t)pb.N * ES : 0u);
+#pragma unroll
+    for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int off = (col0 + 64 * wc + 32 * jn + 8 * g + 4 * hi + r) * ES;
+          if constexpr (BF16) {
+            const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rb, off, 0, 0);
+            bv[jn][g][r] = (float)__builtin_bit_cast(__bf16, h);
+          } else {
+            bv[jn][g][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, off, 0, 0));
+          }
+        }
+  }
+
   const int nkt = K / BK;
   // Two stages: step kt's barrier, after the wait for its own tile, also
   // retires every read of step kt-1, whose slot then receives step kt+1.
@@ -190,18 +213,19 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
   }
 
   // Epilogue: lane holds output row row0 + 64wr + 32im + li and columns
-  // col0 + 64wc + 32jn + 8g + 4hi + {0..3}.
-  const T* bias = reinterpret_cast<const T*>(pb.bias);
+  // col0 + 64wc + 32jn + 8g + 4hi + {0..3}.  Buffer stores with 32-bit
+  // offsets (C stays under 2 GiB): rows past M land past the end of C and
+  // are dropped; columns past N would land in other rows, so they branch.
+  const auto rc = make_rsrc(pb.C, (uint32_t)((size_t)pb.M * pb.N * ES));
 #pragma unroll
   for (int im = 0; im < 2; ++im) {
-    const int row = row0 + 64 * wr + 32 * im + li;
-    if (row >= pb.M) continue;
-    size_t rbase;
+    const uint32_t row = (uint32_t)(row0 + 64 * wr + 32 * im + li);
+    uint32_t rbase;
     if constexpr (C_HEADS) {
-      const int b = row / pb.L, i = row % pb.L;
-      rbase = ((size_t)b * pb.H * pb.L + i) * pb.dk;
+      const uint32_t b = row / (uint32_t)pb.L, i = row % (uint32_t)pb.L;
+      rbase = (b * (uint32_t)pb.H * (uint32_t)pb.L + i) * (uint32_t)pb.dk;
     } else {
-      rbase = (size_t)row * pb.N;
+      rbase = row * (uint32_t)pb.N;
     }
 #pragma unroll
     for (int jn = 0; jn < 2; ++jn)
@@ -209,30 +233,24 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
       for (int g = 0; g < 4; ++g) {
         const int col = col0 + 64 * wc + 32 * jn + 8 * g + 4 * hi;
         if (col >= pb.N) continue;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[jn][im][4 * g + r];
-          if (bias != nullptr) v[r] += (float)bias[col + r];
-        }
-        size_t off;
+        uint32_t off;
         if constexpr (C_HEADS) {
-          const int t = col >> dk_shift, c = col & (pb.dk - 1);
-          off = rbase + (size_t)t * pb.L * pb.dk + c;
+          const uint32_t t = (uint32_t)col >> dk_shift, c = (uint32_t)col & (uint32_t)(pb.dk - 1);
+          off = rbase + t * (uint32_t)pb.L * (uint32_t)pb.dk + c;
         } else {
-          off = rbase + col;
+          off = rbase + (uint32_t)col;
         }
-        T* dst = reinterpret_cast<T*>(pb.C) + off;
+        if (row >= (uint32_t)pb.M) off = (uint32_t)pb.M * (uint32_t)pb.N;  // the end of C: dropped
         if constexpr (BF16) {
           bf16x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = (__bf16)v[r];
-          *reinterpret_cast<bf16x4*>(dst) = o4;
+          for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(acc[jn][im][4 * g + r] + bv[jn][g][r]);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), rc, (int)(off * ES), 0, 0);
         } else {
           f32x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = v[r];
-          *reinterpret_cast<f32x4*>(dst) = o4;
+          for (int r = 0; r < 4; ++r) o4[r] = acc[jn][im][4 * g + r] + bv[jn][g][r];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rc, (int)(off * ES), 0, 0);
         }
       }
   }
