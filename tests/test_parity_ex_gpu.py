@@ -105,6 +105,9 @@ WCASES = [
     (2, 2, 2, 66, 97, 64, "bf16", False, False, None),          # m % 4 != 0
     (1, 2, 1, 65, 131, 128, "f32", "top_left", False, None),    # m % 4 != 0
     (2, 2, 2, 40, 120, 64, "f32", "bottom_right", True, (0, 120)),
+    (2, 4, 2, 100, 256, 128, "bf16", "top_left", True, None),   # m % 8 == 0: staged rows
+    (1, 3, 3, 70, 264, 128, "f32", False, False, (100, 264)),   # staged rows, fp32
+    (2, 2, 1, 33, 132, 64, "bf16", "bottom_right", False, (7, 132)),  # m % 8 == 4
 ]
 
 

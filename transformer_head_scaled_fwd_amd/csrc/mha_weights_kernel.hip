@@ -32,6 +32,7 @@ struct WeightParams {
   int nkb_all;           // key blocks covering m
   int bottom_right;      // causal alignment: 0 top-left, 1 bottom-right
   int vec;               // 1 when m % 4 == 0: four keys per store
+  int vec8;              // 1 when m % 8 == 0: rows staged through LDS, 16-byte stores
   float scale;           // the caller's scale
   float scale_log2;      // scale * log2(e)
 };
@@ -48,7 +49,11 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   constexpr bool BF16 = G::BF16;
   constexpr int BR = G::BR;
   constexpr int NS = P::NS;
-  __shared__ __attribute__((aligned(1024))) char smem[G::NSTAGE * G::TILE];
+  // Staging of one 64-key block of the wave's 32 rows, padded by 16 bytes
+  // per row so that the lanes writing one row each land in distinct banks.
+  constexpr int SROW = BC * ES + 16;
+  constexpr int SWAVE = kRowsPerWave * SROW;
+  __shared__ __attribute__((aligned(1024))) char smem[G::NSTAGE * G::TILE + NW * SWAVE];
   const uint32_t lds_k = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem);
 
@@ -144,6 +149,58 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     }
   };
 
+  // Rows staged through LDS, then stored 16 bytes per lane: each store
+  // instruction writes whole 128-byte row segments (bf16: 8 rows of 64 keys;
+  // fp32: 4 rows) instead of 16 scattered bytes per row.
+  char* stage_w = smem + G::NSTAGE * G::TILE + wave * SWAVE;
+  constexpr int CPRW = BC * ES / 16;    // 16-byte chunks per staged row: 8 (bf16), 16 (fp32)
+  constexpr int RPI = 64 / CPRW;        // rows per store instruction
+  auto store_chunks = [&](int kb, auto&& chunk_of) {
+#pragma unroll
+    for (int rep = 0; rep < kRowsPerWave / RPI; ++rep) {
+      const int rr = rep * RPI + lane / CPRW, c = lane % CPRW;
+      const int key = kb * BC + c * (16 / ES);
+      if (key < m) {
+        const uint32_t off_el = (uint32_t)(row_w + rr) * (uint32_t)m + (uint32_t)key;
+        __builtin_amdgcn_raw_buffer_store_b128(chunk_of(rr, c), ra, (int)(off_el * ES), 0, 0);
+      }
+    }
+  };
+  auto store_block = [&](const f32x16 (&p)[NS], int kb) {
+#pragma unroll
+    for (int jt = 0; jt < NS; ++jt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        char* dst = stage_w + li * SROW + (32 * jt + 8 * g + 4 * hi) * ES;
+        if constexpr (BF16) {
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)p[jt][4 * g + r];
+          *reinterpret_cast<bf16x4*>(dst) = v;
+        } else {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = p[jt][4 * g + r];
+          *reinterpret_cast<f32x4*>(dst) = v;
+        }
+      }
+    // The staging area belongs to this wave alone: order its writes before
+    // the reads below (LDS operations of a wave complete in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    store_chunks(kb, [&](int rr, int c) {
+      return *reinterpret_cast<const u32x4*>(stage_w + rr * SROW + c * 16);
+    });
+    // The next block's writes must not overtake these reads.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto store_zero_block = [&](int kb) {
+    store_chunks(kb, [&](int, int) { return u32x4{0u, 0u, 0u, 0u}; });
+  };
+
   f32x16 zero;
 #pragma unroll
   for (int e = 0; e < 16; ++e) zero[e] = 0.0f;
@@ -167,17 +224,25 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
         if ((kb * BC + BC > L) || (CAUSAL && kb * BC + BC - 1 > prow_w))
           P::mask(s, row_lim - kb * BC - 4 * hi);
 #pragma unroll
-        for (int jt = 0; jt < NS; ++jt) {
+        for (int jt = 0; jt < NS; ++jt)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
             s[jt][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][e], prm.scale_log2, -lse2));
-          store_tile(s[jt], kb, jt);
+        if (prm.vec8) {
+          store_block(s, kb);
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < NS; ++jt) store_tile(s[jt], kb, jt);
         }
+      } else if (prm.vec8) {
+        store_zero_block(kb);
       } else {
 #pragma unroll
         for (int jt = 0; jt < NS; ++jt) store_tile(zero, kb, jt);
       }
       __syncthreads();  // K(kb) is consumed before its slot is refilled
+    } else if (prm.vec8) {
+      store_zero_block(kb);
     } else {
 #pragma unroll
       for (int jt = 0; jt < NS; ++jt) store_tile(zero, kb, jt);
@@ -197,6 +262,7 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.nkb_all = (int)((a.m + BC - 1) / BC);
   prm.bottom_right = a.mode == 2;
   prm.vec = (a.m % 4) == 0;
+  prm.vec8 = (a.m % 8) == 0;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
