@@ -215,44 +215,70 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
   // Epilogue: lane holds output row row0 + 64wr + 32im + li and columns
   // col0 + 64wc + 32jn + 8g + 4hi + {0..3}.  Buffer stores with 32-bit
   // offsets (C stays under 2 GiB): rows past M land past the end of C and
-  // are dropped; columns past N would land in other rows, so they branch.
+  // are dropped; columns past N would land in other rows, so they branch
+  // (N is a multiple of 64, so a wave's 64 columns are all in or all out).
   const auto rc = make_rsrc(pb.C, (uint32_t)((size_t)pb.M * pb.N * ES));
-#pragma unroll
-  for (int im = 0; im < 2; ++im) {
-    const uint32_t row = (uint32_t)(row0 + 64 * wr + 32 * im + li);
-    uint32_t rbase;
+  auto c_off = [&](uint32_t row, uint32_t col) -> uint32_t {
+    if (row >= (uint32_t)pb.M) return (uint32_t)pb.M * (uint32_t)pb.N;  // the end of C: dropped
     if constexpr (C_HEADS) {
       const uint32_t b = row / (uint32_t)pb.L, i = row % (uint32_t)pb.L;
-      rbase = (b * (uint32_t)pb.H * (uint32_t)pb.L + i) * (uint32_t)pb.dk;
+      const uint32_t t = col >> dk_shift, c = col & (uint32_t)(pb.dk - 1);
+      return ((b * (uint32_t)pb.H + t) * (uint32_t)pb.L + i) * (uint32_t)pb.dk + c;
     } else {
-      rbase = row * (uint32_t)pb.N;
+      return row * (uint32_t)pb.N + col;
     }
+  };
+  if constexpr (BF16) {
+    // bf16: the wave's 64 x 64 tile is staged in LDS (the ring is free once
+    // every wave has passed this barrier), rows padded by 16 bytes, and
+    // stored 16 bytes per lane: each instruction writes 8 whole 128-byte
+    // row segments instead of 16 scattered bytes per row.
+    constexpr int SR = 64 * 2 + 16;
+    static_assert(NWAVE * 64 * SR <= NSTAGE * 2 * TILE, "staging must fit the ring");
+    __syncthreads();
+    char* st = smem + wave * 64 * SR;
 #pragma unroll
-    for (int jn = 0; jn < 2; ++jn)
+    for (int im = 0; im < 2; ++im)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = col0 + 64 * wc + 32 * jn + 8 * g + 4 * hi;
-        if (col >= pb.N) continue;
-        uint32_t off;
-        if constexpr (C_HEADS) {
-          const uint32_t t = (uint32_t)col >> dk_shift, c = (uint32_t)col & (uint32_t)(pb.dk - 1);
-          off = rbase + t * (uint32_t)pb.L * (uint32_t)pb.dk + c;
-        } else {
-          off = rbase + (uint32_t)col;
-        }
-        if (row >= (uint32_t)pb.M) off = (uint32_t)pb.M * (uint32_t)pb.N;  // the end of C: dropped
-        if constexpr (BF16) {
+      for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
           bf16x4 o4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) o4[r] = (__bf16)(acc[jn][im][4 * g + r] + bv[jn][g][r]);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o4), rc, (int)(off * ES), 0, 0);
-        } else {
+          *reinterpret_cast<bf16x4*>(st + (32 * im + li) * SR + (32 * jn + 8 * g + 4 * hi) * 2) = o4;
+        }
+    // The staging area belongs to this wave: order its writes before the
+    // reads (LDS operations of a wave complete in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (col0 + 64 * wc < pb.N) {
+#pragma unroll
+      for (int rep = 0; rep < 8; ++rep) {
+        const int rr = rep * 8 + lane / 8, c = lane % 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * SR + c * 16);
+        const uint32_t off = c_off((uint32_t)(row0 + 64 * wr + rr), (uint32_t)(col0 + 64 * wc + 8 * c));
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)(off * ES), 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int im = 0; im < 2; ++im) {
+      const uint32_t row = (uint32_t)(row0 + 64 * wr + 32 * im + li);
+#pragma unroll
+      for (int jn = 0; jn < 2; ++jn)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int col = col0 + 64 * wc + 32 * jn + 8 * g + 4 * hi;
+          if (col >= pb.N) continue;
+          const uint32_t off = c_off(row, (uint32_t)col);
           f32x4 o4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) o4[r] = acc[jn][im][4 * g + r] + bv[jn][g][r];
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rc, (int)(off * ES), 0, 0);
         }
-      }
+    }
   }
 }
 
