@@ -347,23 +347,66 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
                                           (int)((uint32_t)my_row * 4), 0, 0);
   }
+  // O rows staged in LDS when they fit the (now idle) K/V ring, rows padded
+  // by 16 bytes, then stored 16 bytes per lane: each store instruction
+  // writes whole row segments (bf16: 4 rows of d = 128 or 8 of d = 64)
+  // instead of 16 scattered bytes per row.  Every wave has passed the
+  // block loop's last barrier, so no wave still reads the ring (and with no
+  // key block nothing was ever staged there).
+  constexpr int OSR = D * ES + 16;
+  if constexpr (NW * kRowsPerWave * OSR <= G::LDS_BYTES) {
+    char* st = smem + wave * kRowsPerWave * OSR;
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t off = ((uint32_t)my_row * D + ct * 32 + 8 * g + 4 * hi) * ES;
-      if constexpr (BF16) {
-        bf16x4 v;
+      for (int g = 0; g < 4; ++g) {
+        char* dst = st + li * OSR + (ct * 32 + 8 * g + 4 * hi) * ES;
+        if constexpr (BF16) {
+          bf16x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(w.o[ct][4 * g + r] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, (int)off, 0, 0);
-      } else {
-        f32x4 v;
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(w.o[ct][4 * g + r] * inv);
+          *reinterpret_cast<bf16x4*>(dst) = v;
+        } else {
+          f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = w.o[ct][4 * g + r] * inv;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, (int)off, 0, 0);
+          for (int r = 0; r < 4; ++r) v[r] = w.o[ct][4 * g + r] * inv;
+          *reinterpret_cast<f32x4*>(dst) = v;
+        }
       }
+    // The staging area belongs to this wave: order its writes before the
+    // reads (LDS operations of a wave complete in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int CPRO = D * ES / 16;  // 16-byte chunks per row
+    constexpr int RPI = 64 / CPRO;     // rows per store instruction
+#pragma unroll
+    for (int rep = 0; rep < kRowsPerWave / RPI; ++rep) {
+      const int rr = rep * RPI + lane / CPRO, c = lane % CPRO;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * OSR + c * 16);
+      // rows >= n fall outside the O resource and are dropped
+      const uint32_t off = ((uint32_t)(row_w + rr) * D) * ES + c * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
     }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t off = ((uint32_t)my_row * D + ct * 32 + 8 * g + 4 * hi) * ES;
+        if constexpr (BF16) {
+          bf16x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = (__bf16)(w.o[ct][4 * g + r] * inv);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, (int)off, 0, 0);
+        } else {
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = w.o[ct][4 * g + r] * inv;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, (int)off, 0, 0);
+        }
+      }
+  }
 }
 
 template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
