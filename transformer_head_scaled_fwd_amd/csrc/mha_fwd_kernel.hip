@@ -1,8 +1,11 @@
 // mha_fwd_kernel.hip -- fused attention forward for gfx950 (MI355X).
 //
-// One workgroup computes BR = 32 * NW query rows of one (batch, head): NW
-// wave64s, each owning 32 rows.  It walks the key axis in blocks of BC = 64
-// keys.  Per block:
+// One workgroup computes BR query rows of one (batch, head) with NW wave64s,
+// each owning 32 rows.  It walks the key axis in blocks of BC = 64 keys.
+// Usually every wave has rows of its own (BR = 32 NW); on grids too small
+// to give each SIMD more than one wave, the waves form two key groups over
+// the same BR = 16 NW rows, each walking every other key block, and merge
+// their partial softmax sums at the end.  Per block:
 //
 //   stage    K and V blocks -> LDS, row-major, by buffer->LDS direct loads
 //            (no register staging), in a ring of NSTAGE stages so that a
@@ -59,21 +62,24 @@
 
 namespace mha {
 
-// Per-wave state of the key walk: 32 query rows, one per lane pair.
-template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
+// Per-wave state of the key walk: 32 query rows, one per lane pair.  With
+// KS key groups the wave reads key blocks kg, kg + KS, kg + 2 KS, ...: its
+// j-th block is block j KS + kg, held in ring stage j.
+template <typename T, int D, int NW, int KS, bool CAUSAL, bool ALIBI>
 struct Walk {
-  using G = Geo<T, D, NW>;
+  using G = Geo<T, D, NW, KS>;
   using P = Phase<T, D>;
   static constexpr int NS = P::NS;
 
-  const char* ktiles;  // LDS: K ring, NSTAGE tiles
-  const char* vtiles;  // LDS: V ring, NSTAGE tiles
+  const char* ktiles;  // LDS: K ring, NSTAGE stages
+  const char* vtiles;  // LDS: V ring, NSTAGE stages
   int lane, li, hi;
+  int kg;              // key group of the wave
   int prow_w;          // position of the first query row of the wave
   int prow;            // position of this lane's query row
   int row_lim;         // first invalid key of this lane's row
   int L;               // valid keys of the sequence
-  int wave_nkb;        // key blocks this wave reads
+  int wave_nkb;        // key blocks this wave reads (its own, every KS-th)
   float sl2;           // scale * log2(e)
   float sr;            // ALiBi slope / scale (raw-score units)
   u32x4 qf[P::NQF];    // Q fragments
@@ -81,11 +87,17 @@ struct Walk {
   float m_run;         // running max of scale*log2(e)*s (per row)
   float l_run;         // this lane's share of the row sum
 
-  MHA_MEMBER bool needs_mask(int kb) const {
-    return (kb * BC + BC > L) || (CAUSAL && kb * BC + BC - 1 > prow_w);
+  // gb: key block index (keys gb * BC onwards)
+  MHA_MEMBER bool needs_mask(int gb) const {
+    return (gb * BC + BC > L) || (CAUSAL && gb * BC + BC - 1 > prow_w);
   }
-  MHA_MEMBER const char* k_tile(int kb) const { return ktiles + (kb % G::NSTAGE) * G::TILE; }
-  MHA_MEMBER const char* v_tile(int kb) const { return vtiles + (kb % G::NSTAGE) * G::TILE; }
+  // the wave's j-th block: ring stage j % NSTAGE, block kg within the stage
+  MHA_MEMBER const char* k_tile(int j) const {
+    return ktiles + (j % G::NSTAGE) * G::TILE + kg * (BC * G::ROWB);
+  }
+  MHA_MEMBER const char* v_tile(int j) const {
+    return vtiles + (j % G::NSTAGE) * G::TILE + kg * (BC * G::ROWB);
+  }
 
   // Softmax bookkeeping for a block whose raw row max is mx: the running
   // max is raised only when the block max exceeds it by more than TAU.
@@ -111,10 +123,11 @@ struct Walk {
   }
   MHA_MEMBER float msub() const { return (m_run == -__builtin_inff()) ? 0.0f : m_run; }
 
-  // Distance bias and mask of block kb's scores.
-  MHA_MEMBER void bias_and_mask(f32x16 (&s)[NS], int kb) const {
-    if constexpr (ALIBI) P::bias(s, (float)(prow - kb * BC - 4 * hi), sr);
-    if (needs_mask(kb)) P::mask(s, row_lim - kb * BC - 4 * hi);
+  // Distance bias and mask of the scores of the wave's j-th block.
+  MHA_MEMBER void bias_and_mask(f32x16 (&s)[NS], int j) const {
+    const int gb = j * KS + kg;
+    if constexpr (ALIBI) P::bias(s, (float)(prow - gb * BC - 4 * hi), sr);
+    if (needs_mask(gb)) P::mask(s, row_lim - gb * BC - 4 * hi);
   }
 
   // Scores, mask, running max and weights of the first block (prologue).
@@ -127,8 +140,8 @@ struct Walk {
     P::weights(pf, s, sl2, msub(), l_run);
   }
 
-  // PV of block kb (weights in pf_cur) and, when this wave reads block
-  // kb+1, its scores, mask, running max and weights into pf_nxt.
+  // PV of the wave's block kb (weights in pf_cur) and, when the wave reads
+  // a block kb+1, its scores, mask, running max and weights into pf_nxt.
   MHA_MEMBER void step(int kb, const typename P::PFrag& pf_cur, typename P::PFrag& pf_nxt) {
     if (kb + 1 < wave_nkb) {
       f32x16 s[NS];
@@ -167,14 +180,14 @@ constexpr int fwd_wg_per_cu() {
   return (NW == 8 || (sizeof(T) == 4 && D == 128)) ? 1 : 2;
 }
 
-template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
+template <typename T, int D, int NW, int KS, bool CAUSAL, bool ALIBI>
 __global__ void __launch_bounds__(64 * NW, (fwd_wg_per_cu<T, D, NW>()))
 attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
                 const T* __restrict__ Vp, const int32_t* __restrict__ key_lens,
                 const float* __restrict__ alibi_slopes, T* __restrict__ Op,
                 float* __restrict__ lse, FwdParams prm) {
-  using G = Geo<T, D, NW>;
-  using W = Walk<T, D, NW, CAUSAL, ALIBI>;
+  using G = Geo<T, D, NW, KS>;
+  using W = Walk<T, D, NW, KS, CAUSAL, ALIBI>;
   using P = typename W::P;
   constexpr int ES = G::ES;
   constexpr bool BF16 = G::BF16;
@@ -192,6 +205,8 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   w.vtiles = smem + G::NSTAGE * G::TILE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int rg = wave % G::RG;  // row group: query rows 32 rg .. 32 rg + 31
+  w.kg = wave / G::RG;          // key group
   w.lane = tid % 64;
   w.li = w.lane % 32;  // query row within the wave's 32 (MFMA column)
   w.hi = w.lane / 32;  // which half of the k / row groups this lane holds
@@ -227,7 +242,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int b = bh / prm.H, t = bh % prm.H;
   const int bkv = b * (prm.H / prm.group) + t / prm.group;  // K/V head
   const int q0 = qb * BR;
-  const int row_w = q0 + wave * kRowsPerWave;
+  const int row_w = q0 + rg * kRowsPerWave;
   const int my_row = row_w + li;
 
   // Q fragments (MFMA B operand of S^T = K Q^T), kept in registers.  Their
@@ -246,11 +261,14 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // Position of query row i: i + off.
   const int off = (CAUSAL && prm.bottom_right) ? L - n : 0;
   const int kend = CAUSAL ? max(0, min(L, q0 + off + BR)) : L;
-  const int nkb = (kend + BC - 1) / BC;
+  const int nkb = (kend + BC - 1) / BC;  // key blocks of the workgroup
+  const int nst = (nkb + KS - 1) / KS;    // ring stages it walks
   w.prow_w = row_w + off;
   w.prow = my_row + off;
-  // Key blocks any row of this wave can see.
-  w.wave_nkb = CAUSAL ? max(0, min(nkb, (w.prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
+  // Key blocks any row of this wave's row group can see, then those of
+  // them that belong to the wave's key group.
+  const int vis = CAUSAL ? max(0, min(nkb, (w.prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
+  w.wave_nkb = vis > w.kg ? (vis - w.kg + KS - 1) / KS : 0;
   w.row_lim = CAUSAL ? min(L, my_row + off + 1) : L;
   w.sl2 = prm.scale_log2;
   w.sr = ALIBI ? alibi_slopes[t] / prm.scale : 0.0f;
@@ -264,7 +282,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const T* kbase = Kp + head_k;
   const T* vbase = Vp + head_k;
 
-  // Loads of key block j and value block j into their ring slots.
+  // Loads of ring stage j of the keys and of the values into their slots.
   auto load_k = [&](int j) {
     G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
   };
@@ -274,9 +292,9 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 
   // The first key/value blocks, then the wait for Q; the wait before the
   // first barrier below covers the key/value loads.
-  if (nkb > 0) {
-    for (int j = 0; j <= DIST && j < nkb; ++j) load_k(j);
-    for (int j = 0; j < DIST && j < nkb; ++j) load_v(j);
+  if (nst > 0) {
+    for (int j = 0; j <= DIST && j < nst; ++j) load_k(j);
+    for (int j = 0; j < DIST && j < nst; ++j) load_v(j);
   }
   P::pin_q(w.qf);
 
@@ -294,7 +312,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // earlier, i.e. for K(kb+2) and V(kb+1).  Two weight buffers alternate,
   // unrolled by two.
   typename P::PFrag pa, pb;
-  if (nkb > 0) {
+  if (nst > 0) {
     G::template wait_loads<0>();
     __syncthreads();
     if (0 < w.wave_nkb) w.first_block(pa);
@@ -304,10 +322,10 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // Issue this iteration's loads; returns how many tiles were issued.
   auto issue = [&](int kb) -> int {
     int issued = 0;
-    if (kb + DIST < nkb) {
+    if (kb + DIST < nst) {
       load_v(kb + DIST);
       issued = 1;
-      if (kb + 1 + DIST < nkb) {
+      if (kb + 1 + DIST < nst) {
         load_k(kb + 1 + DIST);
         issued = 2;
       }
@@ -326,14 +344,48 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     }
     __syncthreads();
   };
-  for (int kb = 0; kb < nkb; kb += 2) {
+  for (int kb = 0; kb < nst; kb += 2) {
     int issued = issue(kb);
     if (kb < w.wave_nkb) w.step(kb, pa, pb);
     publish(issued);
-    if (kb + 1 >= nkb) break;
+    if (kb + 1 >= nst) break;
     issued = issue(kb + 1);
     if (kb + 1 < w.wave_nkb) w.step(kb + 1, pb, pa);
     publish(issued);
+  }
+
+  // ---- two key groups: key group 1 hands its running max, row-sum share
+  // and unnormalised output to key group 0 through LDS (the ring is idle:
+  // every wave has passed the loop's last barrier, and with no stage walked
+  // nothing was ever staged there).  Both halves are exact partial softmax
+  // sums against their own reference max m_g, so the row's sums are
+  // sum_g 2^(m_g - M) l_g and sum_g 2^(m_g - M) O_g with M = max_g m_g; a
+  // group that saw no valid key has m_g = -inf and contributes 0.
+  constexpr int MERGE_BYTES = KS == 2 ? (2 + (D / 32) * 16) * G::RG * 64 * 4 : 0;
+  if constexpr (KS == 2) {
+    float* mg = reinterpret_cast<float*>(smem);
+    // element e of this lane, row group rg: consecutive lanes, consecutive words
+    auto at = [&](int e) -> float& { return mg[(e * G::RG + rg) * 64 + lane]; };
+    if (w.kg == 1) {
+      at(0) = w.m_run;
+      at(1) = w.l_run;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) at(2 + 16 * t + e) = w.o[t][e];
+    }
+    __syncthreads();
+    if (w.kg == 1) return;
+    const float m1 = at(0), l1 = at(1);
+    const float mx = fmaxf(w.m_run, m1);
+    const float f0 = (w.m_run == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(w.m_run - mx);
+    const float f1 = (m1 == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(m1 - mx);
+    w.l_run = w.l_run * f0 + l1 * f1;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.o[t][e] = w.o[t][e] * f0 + at(2 + 16 * t + e) * f1;
+    w.m_run = mx;
   }
 
   // ---- epilogue: divide by the row sum (0 when no key was valid), store
@@ -347,15 +399,15 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
                                           (int)((uint32_t)my_row * 4), 0, 0);
   }
-  // O rows staged in LDS when they fit the (now idle) K/V ring, rows padded
-  // by 16 bytes, then stored 16 bytes per lane: each store instruction
-  // writes whole row segments (bf16: 4 rows of d = 128 or 8 of d = 64)
-  // instead of 16 scattered bytes per row.  Every wave has passed the
-  // block loop's last barrier, so no wave still reads the ring (and with no
-  // key block nothing was ever staged there).
+  // O rows staged in LDS when they fit the (now idle) K/V ring, past the
+  // merge area, rows padded by 16 bytes, then stored 16 bytes per lane:
+  // each store instruction writes whole row segments (bf16: 4 rows of
+  // d = 128 or 8 of d = 64) instead of 16 scattered bytes per row.  Every
+  // wave has passed the block loop's last barrier, so no wave still reads
+  // the ring (and with no key block nothing was ever staged there).
   constexpr int OSR = D * ES + 16;
-  if constexpr (NW * kRowsPerWave * OSR <= G::LDS_BYTES) {
-    char* st = smem + wave * kRowsPerWave * OSR;
+  if constexpr (MERGE_BYTES + G::RG * kRowsPerWave * OSR <= G::LDS_BYTES) {
+    char* st = smem + MERGE_BYTES + rg * kRowsPerWave * OSR;
 #pragma unroll
     for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
@@ -409,9 +461,9 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   }
 }
 
-template <typename T, int D, int NW, bool CAUSAL, bool ALIBI>
+template <typename T, int D, int NW, int KS, bool CAUSAL, bool ALIBI>
 static hipError_t launch_one(const LaunchArgs& a) {
-  constexpr int BR = Geo<T, D, NW>::BR;
+  constexpr int BR = Geo<T, D, NW, KS>::BR;
   FwdParams prm;
   prm.H = (int)a.H;
   prm.group = (int)(a.H / a.H_kv);
@@ -437,31 +489,43 @@ static hipError_t launch_one(const LaunchArgs& a) {
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, CAUSAL, ALIBI>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, KS, CAUSAL, ALIBI>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K,
                      (const T*)a.V, a.key_lens, a.alibi_slopes, (T*)a.O, a.lse, prm);
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int KS>
 static hipError_t launch_variant(const LaunchArgs& a) {
   const bool causal = a.mode != 0;
   if (a.alibi_slopes != nullptr)
-    return causal ? launch_one<T, D, NW, true, true>(a) : launch_one<T, D, NW, false, true>(a);
-  return causal ? launch_one<T, D, NW, true, false>(a) : launch_one<T, D, NW, false, false>(a);
+    return causal ? launch_one<T, D, NW, KS, true, true>(a) : launch_one<T, D, NW, KS, false, true>(a);
+  return causal ? launch_one<T, D, NW, KS, true, false>(a) : launch_one<T, D, NW, KS, false, false>(a);
 }
 
-// Workgroup size: 8 waves (256 query rows, one workgroup per CU) for bf16
-// with d = 128 when the query axis gives every CU several workgroups;
-// otherwise 4 waves (128 rows, two workgroups per CU).
+// Workgroup shape:
+//  - 8 waves as 8 row groups (256 query rows, one workgroup per CU) for bf16
+//    with d = 128 when the query axis gives every CU several workgroups;
+//  - 8 waves as 4 row groups x 2 key groups (128 rows) for bf16 when 128-row
+//    workgroups would leave one wave per SIMD (at most one workgroup per CU)
+//    and the key axis is long (m >= 1024): one wave would walk all of it
+//    serially, and splitting the walk halves the chain of dependent blocks.
+//    The merge at the end costs about as much as three blocks of the walk,
+//    so shorter walks keep one key group (measured: m = 256 and 512 lose
+//    4-11%, m = 1024, 2048 and 4096 gain 4%, 9% and 12%);
+//  - otherwise 4 waves (128 rows, two workgroups per CU).
 template <typename T, int D>
 static hipError_t launch_d(const LaunchArgs& a) {
-  if constexpr (D == 128 && sizeof(T) == 2) {
-    const int64_t big_blocks = ((a.n + 255) / 256) * a.B * a.H;
-    if (big_blocks >= 4 * 256 && big_blocks <= (int64_t)UINT32_MAX / 512)
-      return launch_variant<T, D, 8>(a);
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (D == 128) {
+      const int64_t big_blocks = ((a.n + 255) / 256) * a.B * a.H;
+      if (big_blocks >= 4 * 256 && big_blocks <= (int64_t)UINT32_MAX / 512)
+        return launch_variant<T, D, 8, 1>(a);
+    }
+    const int64_t blocks = ((a.n + 127) / 128) * a.B * a.H;
+    if (blocks <= 256 && a.m >= 16 * BC) return launch_variant<T, D, 8, 2>(a);
   }
-  return launch_variant<T, D, 4>(a);
+  return launch_variant<T, D, 4, 1>(a);
 }
 
 template <typename T>

@@ -76,16 +76,21 @@ struct Swz {
   }
 };
 
-// Tile geometry and LDS ring.  ES: element bytes; NW: waves per workgroup.
-template <typename T, int D, int NW>
+// Tile geometry and LDS ring.  ES: element bytes; NW: waves per workgroup;
+// KS: key groups per workgroup (the waves form NW / KS row groups of 32
+// query rows, and key group g of a row group takes the g-th of every KS
+// consecutive key blocks, so one ring stage holds KS blocks).
+template <typename T, int D, int NW, int KS = 1>
 struct Geo {
   using S = Swz<T, D>;
   static constexpr int ES = sizeof(T);
   static constexpr bool BF16 = (ES == 2);
-  static constexpr int BR = kRowsPerWave * NW;  // query rows per workgroup
+  static constexpr int RG = NW / KS;            // row groups
+  static constexpr int BR = kRowsPerWave * RG;  // query rows per workgroup
   static constexpr int ROWB = D * ES;           // bytes per K or V row in LDS
   static constexpr int CPR = ROWB / 16;         // chunks per row
-  static constexpr int TILE = BC * ROWB;        // one K or one V block
+  static constexpr int TILE = KS * BC * ROWB;   // KS K or V blocks (one ring stage)
+  static_assert(NW % KS == 0, "waves must split evenly into key groups");
   // Two stages: a block is loaded one block ahead of its use.  (A third
   // stage, loading two blocks ahead, measured slower: the loads already land
   // within one block's compute, and the ring index costs more.)
@@ -96,11 +101,13 @@ struct Geo {
   static constexpr int LOADS = TILE / 1024 / NW;
   static_assert(TILE % (1024 * NW) == 0, "tile must split into 1 KiB loads per wave");
 
-  // Direct loads of one key or value block (block kb, rows at or beyond
-  // `bytes` read as 0) into the tile at LDS address `tile`.  Load u of a
-  // wave fills bytes [1 KiB * (u * NW + wave), +1 KiB) of the tile; lane t
-  // writes the 16 bytes at +16t, i.e. chunk position pc of row r, which
-  // holds global chunk pc ^ swizzle(r).
+  // Direct loads of one ring stage of keys or values (rows KS * BC * kb
+  // onwards, rows at or beyond `bytes` read as 0) into the tile at LDS
+  // address `tile`.  Load u of a wave fills bytes [1 KiB * (u * NW + wave),
+  // +1 KiB) of the tile; lane t writes the 16 bytes at +16t, i.e. chunk
+  // position pc of row r, which holds global chunk pc ^ swizzle(r).  The
+  // swizzles repeat every 16 rows, so each BC-row block of a stage is laid
+  // out as a stand-alone tile would be.
   //
   // The loads are issued from inline assembly (M0 set in the same statement)
   // so that the compiler's wait-count pass does not treat every later LDS
@@ -117,7 +124,7 @@ struct Geo {
       const int q = slot + lane;
       const int r = q / CPR, pc = q % CPR;
       const uint32_t off =
-          ((uint32_t)(kb * BC + r) * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
+          ((uint32_t)(kb * KS * BC + r) * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
     }
