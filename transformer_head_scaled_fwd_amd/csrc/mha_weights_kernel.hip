@@ -10,12 +10,14 @@
 // Unlike the forward pass this materialises B*H*n*m elements; it is the
 // optional, memory-bound companion of the forward kernel, not part of it.
 //
-// One workgroup (4 waves, 128 query rows) of one (batch, head) walks every
-// key block of the row range: blocks that hold a visible key get S^T = K Q^T
-// on MFMA (K staged through the direct-load ring, one block ahead), the
-// distance bias, the mask and the exponent; blocks past the last visible key
-// are written as zeros without reading K.  Each lane holds one query row and
-// stores 4 consecutive keys at a time.
+// One workgroup (4 waves, 128 query rows) of one (batch, head) walks one
+// chunk of consecutive key blocks: blocks that hold a visible key get
+// S^T = K Q^T on MFMA (K staged through the direct-load ring, one block
+// ahead), the distance bias, the mask and the exponent; blocks past the last
+// visible key are written as zeros without reading K.  The weights of
+// different key blocks are independent, so the key axis is cut into as many
+// chunks (workgroups) as it takes to give every CU several workgroups; no
+// result is combined across chunks.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,6 +32,7 @@ struct WeightParams {
   int n, m;              // query rows, key rows per head
   int nqb;               // query blocks per head
   int nkb_all;           // key blocks covering m
+  int kchunk;            // key blocks per workgroup (one chunk)
   int bottom_right;      // causal alignment: 0 top-left, 1 bottom-right
   int vec;               // 1 when m % 4 == 0: four keys per store
   int vec8;              // 1 when m % 8 == 0: rows staged through LDS, 16-byte stores
@@ -61,8 +64,13 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, li = lane % 32, hi = lane / 32;
   const int n = prm.n, m = prm.m;
-  const int BH = gridDim.x / prm.nqb;
-  const int bh = blockIdx.x % BH, qb = blockIdx.x / BH;
+  // Workgroup index: (chunk, query block, batch * head), the last fastest.
+  const int nkc = (prm.nkb_all + prm.kchunk - 1) / prm.kchunk;
+  const int BH = gridDim.x / (prm.nqb * nkc);
+  const int bh = blockIdx.x % BH, qb = (blockIdx.x / BH) % prm.nqb;
+  const int kc = blockIdx.x / (BH * prm.nqb);
+  const int kb0 = kc * prm.kchunk;                      // this chunk's key blocks
+  const int kb1 = min(prm.nkb_all, kb0 + prm.kchunk);   // [kb0, kb1)
   const int b = bh / prm.H, t = bh % prm.H;
   const int bkv = b * (prm.H / prm.group) + t / prm.group;
   const int q0 = qb * BR;
@@ -75,6 +83,7 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int off = (CAUSAL && prm.bottom_right) ? L - n : 0;
   const int kend = CAUSAL ? max(0, min(L, q0 + off + BR)) : L;
   const int nkb = (kend + BC - 1) / BC;  // blocks with a visible key for some row
+  const int kvis = min(nkb, kb1);        // this chunk's visible blocks end here
   const int row_w = q0 + wave * kRowsPerWave;
   const int prow_w = row_w + off;
   const int wave_nkb = CAUSAL ? max(0, min(nkb, (prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
@@ -100,7 +109,7 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   auto load_k = [&](int j) {
     G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
   };
-  if (nkb > 0) load_k(0);
+  if (kb0 < kvis) load_k(kb0);
 
   u32x4 qf[P::NQF];
   P::load_q(qf, rq, my_row, hi);
@@ -205,12 +214,12 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 #pragma unroll
   for (int e = 0; e < 16; ++e) zero[e] = 0.0f;
 
-  for (int kb = 0; kb < prm.nkb_all; ++kb) {
-    if (kb < nkb) {
+  for (int kb = kb0; kb < kb1; ++kb) {
+    if (kb < kvis) {
       // K(kb) was requested one block ago; request K(kb+1) into the other
       // slot (last read before the barrier that ended block kb-1), then wait
       // for K(kb) only.
-      if (kb + 1 < nkb) {
+      if (kb + 1 < kvis) {
         load_k(kb + 1);
         G::template wait_loads<G::LOADS>();
       } else {
@@ -260,12 +269,19 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.m = (int)a.m;
   prm.nqb = (int)((a.n + BR - 1) / BR);
   prm.nkb_all = (int)((a.m + BC - 1) / BC);
+  // Key chunks: enough workgroups for about four per CU (a workgroup walks
+  // its chunk's blocks serially, one wave per SIMD each), but whole blocks.
+  const int64_t units = (int64_t)((a.n + BR - 1) / BR) * a.B * a.H;
+  const int64_t want = (4 * 256 + units - 1) / units;
+  const int64_t nkc0 = want < 1 ? 1 : (want > prm.nkb_all ? prm.nkb_all : want);
+  prm.kchunk = prm.nkb_all > 0 ? (int)((prm.nkb_all + nkc0 - 1) / nkc0) : 1;
+  const int64_t nkc = prm.nkb_all > 0 ? (prm.nkb_all + prm.kchunk - 1) / prm.kchunk : 1;
   prm.bottom_right = a.mode == 2;
   prm.vec = (a.m % 4) == 0;
   prm.vec8 = (a.m % 8) == 0;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
-  const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
+  const int64_t blocks = units * nkc;
   hipLaunchKernelGGL((attn_weights_kernel<T, D, CAUSAL, ALIBI>), dim3((unsigned)blocks), dim3(256),
                      0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, a.key_lens,
                      a.alibi_slopes, a.lse, (T*)a.A, prm);
