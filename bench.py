@@ -242,7 +242,7 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     kern = statistics.mean(per)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     return {
-        "workload": name, "dtype": w.dtype, "B": w.B, "H": w.H, "n": w.n, "m": w.m,
+        "workload": name, "dtype": w.dtype, "seed": w.seed, "B": w.B, "H": w.H, "n": w.n, "m": w.m,
         "d": w.d, "causal": w.causal, "key_lens": None if w.lens is None else list(w.lens),
         "input_sets": len(sets), "launches": steps,
         "ms_per_launch": avg, "kernel_ms_mean": kern, "kernel_ms_median": statistics.median(per),
