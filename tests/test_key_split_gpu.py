@@ -53,6 +53,10 @@ CASES = [
     (3, 2, 2, 70, 1024, 64, False, True, (1, 1024)),         # ragged, the last of one key
     (1, 3, 3, 129, 1088, 64, False, False, (1025, 1088)),    # length past a stage boundary
     (2, 2, 1, 5, 4000, 128, "bottom_right", False, (64, 4000)),
+    # B * H_kv a multiple of 8 with grouped heads: each K/V head's workgroups
+    # are pinned to one XCD as well
+    (8, 8, 2, 100, 1100, 64, False, False, (500, 1100)),
+    (8, 4, 1, 64, 1024, 128, "bottom_right", True, (900, 1024)),
 ]
 
 
