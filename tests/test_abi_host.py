@@ -103,6 +103,19 @@ def test_huge_sizes_are_rejected_not_wrapped(lib):
         assert val(lib, **dict(BIG, **kw)) == UNSUP, kw
 
 
+def test_empty_query_axis_with_huge_batch_is_ok(lib):
+    # With n = 0 there is nothing to compute and no grid to bound B * H; the
+    # byte extents of K and V (B * H * m * d elements) exceed 64 bits and
+    # must saturate in the check rather than wrap.
+    huge = dict(B=(1 << 31) - 1, H=(1 << 31) - 1, n=0, m=(1 << 23) - 1, dk=128, dv=128)
+    assert val(lib, **dict(BIG, **huge)) == OK
+    assert val_ex(lib, **dict(BIG, lse=5 << 40, kl=6 << 40, Hkv=huge["H"], **huge)) == OK
+    assert val_w(lib, q=1 << 40, k=2 << 40, lse=5 << 40, a=4 << 40, kl=6 << 40,
+                 B=huge["B"], H=huge["H"], Hkv=huge["H"], n=0, m=huge["m"], dk=128) == OK
+    # and the same batch with one query row is refused by the grid bound
+    assert val(lib, **dict(BIG, **dict(huge, n=1))) == UNSUP
+
+
 def test_q_k_v_may_alias_each_other(lib):
     assert val(lib, k=Q, v=Q) == OK
 

@@ -29,6 +29,12 @@ int64_t mul_sat(int64_t a, int64_t b) {
   return a > INT64_MAX / b ? INT64_MAX : a * b;
 }
 
+// Byte extent a * b * c * d of a tensor, saturating: with an empty query
+// axis nothing else bounds the batch and head counts.
+int64_t extent(int64_t a, int64_t b, int64_t c, int64_t d) {
+  return mul_sat(mul_sat(mul_sat(a, b), c), d);
+}
+
 // Whether `count` elements of `bytes_each` bytes stay under kMaxHeadBytes.
 bool head_fits(int64_t count, int64_t bytes_each) {
   return count <= (kMaxHeadBytes - 1) / bytes_each;
@@ -57,22 +63,23 @@ int check_forward(const void* Q, const void* K, const void* V, const int32_t* ke
   // waves over 256 rows only where that grid fits as well).
   if (B > INT32_MAX || H > INT32_MAX) return MHA_ERR_UNSUPPORTED;
   if (!grid_fits(mul_sat(mul_sat((n + 127) / 128, B), H), 256)) return MHA_ERR_UNSUPPORTED;
-  const int64_t q_bytes = B * H * n * d_k * es;
-  const int64_t kv_bytes = B * H_kv * m * d_k * es;
-  const int64_t o_bytes = B * H * n * d_v * es;
-  const int64_t lse_bytes = lse ? B * H * n * 4 : 0;
+  const int64_t q_bytes = extent(B, H, n, d_k * es);
+  const int64_t kv_bytes = extent(B, H_kv, m, d_k * es);
+  const int64_t o_bytes = extent(B, H, n, d_v * es);
+  const int64_t lse_bytes = lse ? extent(B, H, n, 4) : 0;
   const int64_t alibi_bytes = alibi ? H * 4 : 0;
+  const int64_t lens_bytes = mul_sat(B, 4);
   if ((q_bytes > 0 && Q == nullptr) || (kv_bytes > 0 && (K == nullptr || V == nullptr)) ||
       (o_bytes > 0 && O == nullptr))
     return MHA_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return MHA_ERR_ALIGN;
   if (((uintptr_t)lse & 3u) || ((uintptr_t)alibi & 3u)) return MHA_ERR_ALIGN;
   if (overlaps(O, o_bytes, Q, q_bytes) || overlaps(O, o_bytes, K, kv_bytes) ||
-      overlaps(O, o_bytes, V, kv_bytes) || overlaps(O, o_bytes, key_lens, 4 * B) ||
+      overlaps(O, o_bytes, V, kv_bytes) || overlaps(O, o_bytes, key_lens, lens_bytes) ||
       overlaps(O, o_bytes, alibi, alibi_bytes) || overlaps(O, o_bytes, lse, lse_bytes))
     return MHA_ERR_ALIAS;
   if (overlaps(lse, lse_bytes, Q, q_bytes) || overlaps(lse, lse_bytes, K, kv_bytes) ||
-      overlaps(lse, lse_bytes, V, kv_bytes) || overlaps(lse, lse_bytes, key_lens, 4 * B) ||
+      overlaps(lse, lse_bytes, V, kv_bytes) || overlaps(lse, lse_bytes, key_lens, lens_bytes) ||
       overlaps(lse, lse_bytes, alibi, alibi_bytes))
     return MHA_ERR_ALIAS;
   return MHA_OK;
@@ -182,17 +189,18 @@ int mha_validate_weights(const void* Q, const void* K, const int32_t* key_lens, 
   if (n > 0 && m > 0 && !head_fits(mul_sat(n, m), es)) return MHA_ERR_UNSUPPORTED;
   if (B > INT32_MAX || H > INT32_MAX || !grid_fits(mul_sat(mul_sat((n + 127) / 128, B), H), 256))
     return MHA_ERR_UNSUPPORTED;
-  const int64_t q_bytes = B * H * n * d_k * es;
-  const int64_t k_bytes = B * H_kv * m * d_k * es;
-  const int64_t a_bytes = B * H * n * m * es;
-  const int64_t lse_bytes = B * H * n * 4;
+  const int64_t q_bytes = extent(B, H, n, d_k * es);
+  const int64_t k_bytes = extent(B, H_kv, m, d_k * es);
+  const int64_t a_bytes = extent(B, H, mul_sat(n, m), es);
+  const int64_t lse_bytes = extent(B, H, n, 4);
   const int64_t alibi_bytes = alibi_slopes ? H * 4 : 0;
   if (a_bytes > 0 && (Q == nullptr || K == nullptr || lse == nullptr || A == nullptr))
     return MHA_ERR_NULL;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(A)) return MHA_ERR_ALIGN;
   if (((uintptr_t)lse & 3u) || ((uintptr_t)alibi_slopes & 3u)) return MHA_ERR_ALIGN;
   if (overlaps(A, a_bytes, Q, q_bytes) || overlaps(A, a_bytes, K, k_bytes) ||
-      overlaps(A, a_bytes, key_lens, 4 * B) || overlaps(A, a_bytes, alibi_slopes, alibi_bytes) ||
+      overlaps(A, a_bytes, key_lens, mul_sat(B, 4)) ||
+      overlaps(A, a_bytes, alibi_slopes, alibi_bytes) ||
       overlaps(A, a_bytes, lse, lse_bytes))
     return MHA_ERR_ALIAS;
   return MHA_OK;
@@ -262,13 +270,13 @@ int mha_validate_decode(const void* Q, const void* K, const void* V, const int32
     if (workspace == nullptr || workspace_bytes < p.workspace_bytes || !aligned16(workspace))
       return MHA_ERR_WORKSPACE;
     const int64_t wb = p.workspace_bytes;
-    const int64_t q_bytes = B * H * n * d_k * es;
-    const int64_t kv_bytes = B * H_kv * m * d_k * es;
+    const int64_t q_bytes = extent(B, H, n, d_k * es);
+    const int64_t kv_bytes = extent(B, H_kv, m, d_k * es);
     if (overlaps(workspace, wb, Q, q_bytes) || overlaps(workspace, wb, K, kv_bytes) ||
         overlaps(workspace, wb, V, kv_bytes) || overlaps(workspace, wb, O, q_bytes) ||
-        overlaps(workspace, wb, cache_lens, 4 * B) ||
+        overlaps(workspace, wb, cache_lens, mul_sat(B, 4)) ||
         overlaps(workspace, wb, alibi_slopes, alibi_slopes ? 4 * H : 0) ||
-        overlaps(workspace, wb, lse, lse ? 4 * B * H * n : 0))
+        overlaps(workspace, wb, lse, lse ? extent(B, H, n, 4) : 0))
       return MHA_ERR_WORKSPACE;
   }
   return MHA_OK;
