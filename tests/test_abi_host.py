@@ -156,6 +156,14 @@ def test_forward_refuses_cpu_tensors():
         mha.forward(q, q, q)
 
 
+def test_multihead_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    W = torch.zeros(64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mha.multihead_forward(x, x, x, W, None, W, None, W, None, W, None, 1)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mha, "_lib", None)
     monkeypatch.setattr(mha, "LIB_PATH", str(tmp_path / "absent.so"))

@@ -134,3 +134,11 @@ def test_decode_at_the_per_head_limit(gpu):
     assert maxerr(o.cpu(), ref, "O") <= TOL_O["bf16"]
     del k, v, o
     torch.cuda.empty_cache()
+
+
+def test_decode_binding_rejects_host_workspace(gpu):
+    q, k, v, kl = draw(4, 32, 8, 1, 4096, 128, "bf16", seed=12, lens=(1000, 4096))
+    host_ws = torch.empty(1 << 22, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mha.decode(q.to(DEV), k.to(DEV), v.to(DEV), cache_lens=torch.as_tensor(kl).to(DEV),
+                   workspace=host_ws)

@@ -119,3 +119,22 @@ def test_multihead_workload_sampled(gpu, name):
         err = np.abs(oracle.to_f64(y[sl]) - y_ref).max()
         _say("batch %d Y max_abs_err=%.3e" % (b, err))
         assert err <= tol_y(w.dtype, y_ref)
+
+
+def test_multihead_binding_rejects_bad_out_and_workspace(gpu):
+    # The library sees only addresses: an output of the wrong size or a
+    # workspace in host memory must be refused by the binding, before any
+    # launch.
+    xq, xk, xv, Ws, bs = layer_inputs(1, 16, 16, 128, "bf16", seed=5)
+    d = lambda t: None if t is None else t.to(DEV)  # noqa: E731
+    args = [d(xq), d(xk), d(xv), d(Ws[0]), d(bs[0]), d(Ws[1]), d(bs[1]), d(Ws[2]), d(bs[2]),
+            d(Ws[3]), d(bs[3]), 2]
+    small = torch.empty((1, 8, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        mha.multihead_forward(*args, out=small)
+    host_ws = torch.empty(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mha.multihead_forward(*args, workspace=host_ws)
+    y = mha.multihead_forward(*args)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (1, 16, 128)

@@ -311,6 +311,14 @@ def attention_weights(q, k, lse, key_lens=None, causal=False, alibi_slopes=None,
     return out
 
 
+def _workspace(workspace, dev):
+    """A caller's workspace must be contiguous device memory on the GPU of the
+    other tensors: the library only sees its address and size."""
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    return workspace
+
+
 def decode_workspace_size(B, H, H_kv, n, m, d, dtype_code) -> int:
     """Bytes of workspace mha_decode needs for these sizes (0: none)."""
     out = ctypes.c_int64(0)
@@ -340,6 +348,7 @@ def decode(q, k_cache, v_cache, cache_lens=None, alibi_slopes=None, scale=None,
         raise ValueError("out must be a contiguous [B, H, n, d_v] tensor like q")
     lse = torch.empty((B, H, n), dtype=torch.float32, device=dev) if return_lse else None
     need = decode_workspace_size(B, H, Hkv, n, m, dk, code)
+    workspace = _workspace(workspace, dev)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = None if workspace is None else workspace.data_ptr()
@@ -377,6 +386,10 @@ def multihead_forward(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, num_heads,
     lib = load()
     code = _dtype_code(xq)
     dev = xq.device
+    if dev.type != "cuda":
+        raise ValueError("the tensors must be on a GPU")
+    if xq.dim() != 3 or xk.dim() != 3 or xv.dim() != 3:
+        raise ValueError("xq, xk, xv must be 3-D [B, L, d_model]")
     tensors = [xq, xk, xv, Wq, Wk, Wv, Wo] + [b for b in (bq, bk, bv, bo) if b is not None]
     for t in tensors:
         if t.dtype != xq.dtype or t.device != dev or not t.is_contiguous():
@@ -394,14 +407,18 @@ def multihead_forward(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, num_heads,
     kl_ptr = None
     if key_lens is not None:
         if key_lens.dtype != torch.int32 or key_lens.device != dev or \
-                tuple(key_lens.shape) != (B,):
-            raise ValueError("key_lens must be an int32 tensor [B] on the GPU of xq")
+                tuple(key_lens.shape) != (B,) or not key_lens.is_contiguous():
+            raise ValueError("key_lens must be a contiguous int32 tensor [B] on the GPU of xq")
         kl_ptr = key_lens.data_ptr()
     H = int(num_heads)
     if out is None:
         out = torch.empty((B, n, dm), dtype=xq.dtype, device=dev)
+    elif tuple(out.shape) != (B, n, dm) or out.dtype != xq.dtype or out.device != dev \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, n, d_model] tensor like xq")
     A = torch.empty((B, H, n, m), dtype=xq.dtype, device=dev) if need_weights else None
     need = multihead_workspace_size(B, n, m, dm, H, code, need_weights)
+    workspace = _workspace(workspace, dev)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     sc = default_scale(dm // H) if scale is None else float(scale)
