@@ -21,9 +21,12 @@
 //            n queries are the last tokens of a sequence of L_b, as in
 //            decoding against a key/value cache);
 //   softmax  online: running row max and sum in fp32, exp2 with the scale
-//            and log2(e) folded into one FMA, rescale of the output only when
-//            the row max grew by more than 2^TAU ("Transformer" wiki page:
-//            mixed precision needs the blockwise, online softmax);
+//            and log2(e) folded into one FMA ("Transformer" wiki page: mixed
+//            precision needs the blockwise, online softmax).  A block's
+//            weights are taken against the running max as it stands; only
+//            when one of them could exceed 2^16 (its lane's block sum does)
+//            is the block max formed, the running max raised and the output
+//            rescaled;
 //   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype; the V
 //            operand comes straight from the row-major tile through the
 //            LDS transpose read (ds_read_b64_tr_b16).
@@ -99,8 +102,10 @@ struct Walk {
     return vtiles + (j % G::NSTAGE) * G::TILE + kg * (BC * G::ROWB);
   }
 
-  // Softmax bookkeeping for a block whose raw row max is mx: the running
-  // max is raised only when the block max exceeds it by more than TAU.
+  // Softmax bookkeeping for a block whose raw row max is mx (the first
+  // block, and blocks whose weights against the running max grew too
+  // large): the running max is raised only when the block max exceeds it by
+  // more than TAU.
   // Returns the factor alpha by which earlier sums and outputs must be
   // multiplied (1 when the max stays); the sum is rescaled here, the output
   // by the caller once the PV MFMAs that still add to it have been issued.
@@ -149,11 +154,24 @@ struct Walk {
       P::prefetch_k();
       bias_and_mask(s, kb + 1);
       P::pv(o, v_tile(kb), pf_cur, lane);
-      bool grew;
-      const float alpha = raise_max(pair_max(P::lane_max(s)), grew);
-      P::weights(pf_nxt, s, sl2, msub(), l_run);
+      // Weights against the running max as it stands.  Every weight is at
+      // most the lane's block sum, so while no lane's sum exceeds 2^16 the
+      // running max can stay; otherwise (or for a row whose first valid key
+      // is in this block) the whole wave takes the exact path: raise the
+      // max, recompute the weights, rescale.
+      float lb = 0.0f;
+      P::weights(pf_nxt, s, sl2, msub(), lb);
       P::pin(pf_nxt);
-      rescale_output(alpha, grew);
+      const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && lb > 0.0f);
+      if (__any(slow)) {
+        bool grew;
+        const float alpha = raise_max(pair_max(P::lane_max(s)), grew);
+        lb = 0.0f;
+        P::weights(pf_nxt, s, sl2, msub(), lb);
+        P::pin(pf_nxt);
+        rescale_output(alpha, grew);
+      }
+      l_run += lb;
     } else {
       P::pv(o, v_tile(kb), pf_cur, lane);
     }

@@ -27,7 +27,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRowsPerWave = 32;
 constexpr int BC = 64;  // keys per block
 // The running max used for exp2 is raised only when a row's max exceeds it
-// by more than TAU (log2 units), so unnormalised weights stay below 2^TAU.
+// by more than TAU (log2 units), so right after a raise the unnormalised
+// weights stay below 2^TAU.  (The forward kernel forms the block max only
+// when a weight could exceed 2^16; see its key walk.)
 constexpr float TAU = 8.0f;
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
