@@ -26,7 +26,8 @@
 //            weights are taken against the running max as it stands; only
 //            when one of them could exceed 2^16 (its lane's block sum does)
 //            is the block max formed, the running max raised and the output
-//            rescaled;
+//            rescaled.  With a distance bias, whose row max rises block after
+//            block towards the diagonal, the block max is formed every block;
 //   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype; the V
 //            operand comes straight from the row-major tile through the
 //            LDS transpose read (ds_read_b64_tr_b16).
@@ -154,6 +155,16 @@ struct Walk {
       P::prefetch_k();
       bias_and_mask(s, kb + 1);
       P::pv(o, v_tile(kb), pf_cur, lane);
+      if constexpr (ALIBI) {
+        // A distance bias raises the row max block after block on the way
+        // to the diagonal: form the block max every block.
+        bool grew;
+        const float alpha = raise_max(pair_max(P::lane_max(s)), grew);
+        P::weights(pf_nxt, s, sl2, msub(), l_run);
+        P::pin(pf_nxt);
+        rescale_output(alpha, grew);
+        return;
+      }
       // Weights against the running max as it stands.  Every weight is at
       // most the lane's block sum, so while no lane's sum exceeds 2^16 the
       // running max can stay; otherwise (or for a row whose first valid key
