@@ -345,7 +345,10 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     G::template wait_loads<0>();
     __syncthreads();
     if (0 < w.wave_nkb) w.first_block(pa);
-    __syncthreads();  // K(0) is consumed before its slot is refilled
+    // K(0) is consumed before its slot is refilled, by the load of stage
+    // 1 + NSTAGE - 1 in the first iteration; a walk of at most NSTAGE
+    // stages never refills it.
+    if (nst > G::NSTAGE) __syncthreads();
   }
 
   // Issue this iteration's loads; returns how many tiles were issued.
