@@ -87,6 +87,7 @@ struct Walk {
   float sl2;           // scale * log2(e)
   float sr;            // ALiBi slope / scale (raw-score units)
   u32x4 qf[P::NQF];    // Q fragments
+  uint32_t ko[P::NKO]; // K operand offsets within a tile (bf16)
   f32x16 o[D / 32];    // O^T accumulator
   float m_run;         // running max of scale*log2(e)*s (per row)
   float l_run;         // this lane's share of the row sum
@@ -148,13 +149,22 @@ struct Walk {
 
   // PV of the wave's block kb (weights in pf_cur) and, when the wave reads
   // a block kb+1, its scores, mask, running max and weights into pf_nxt.
+  //
+  // ST = kb % NSTAGE, a constant in the loop (unrolled by the ring depth), so
+  // that with the precomputed K offsets every tile read is a register plus
+  // an immediate offset.
+  template <int ST>
   MHA_MEMBER void step(int kb, const typename P::PFrag& pf_cur, typename P::PFrag& pf_nxt) {
+    const int kgo = KS == 1 ? 0 : kg * (BC * G::ROWB);
+    const char* kt_next = ktiles + ((ST + 1) % G::NSTAGE) * G::TILE + kgo;
+    const char* vt_cur = vtiles + ST * G::TILE + kgo;
     if (kb + 1 < wave_nkb) {
       f32x16 s[NS];
-      P::scores(s, k_tile(kb + 1), qf, li, hi);
+      if constexpr (G::BF16) P::scores_ko(s, kt_next, qf, ko);
+      else P::scores(s, kt_next, qf, li, hi);
       P::prefetch_k();
       bias_and_mask(s, kb + 1);
-      P::pv(o, v_tile(kb), pf_cur, lane);
+      P::pv(o, vt_cur, pf_cur, lane);
       if constexpr (ALIBI) {
         // A distance bias raises the row max block after block on the way
         // to the diagonal: form the block max every block.
@@ -184,7 +194,7 @@ struct Walk {
       }
       l_run += lb;
     } else {
-      P::pv(o, v_tile(kb), pf_cur, lane);
+      P::pv(o, vt_cur, pf_cur, lane);
     }
   }
 };
@@ -333,6 +343,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     for (int e = 0; e < 16; ++e) w.o[t][e] = 0.0f;
   w.m_run = -__builtin_inff();
   w.l_run = 0.0f;
+  if constexpr (BF16) P::k_offsets(w.ko, li, hi);
 
   // Pipeline: iteration kb reads K(kb+1) and V(kb).  It issues the loads of
   // K(kb+1+DIST) and V(kb+DIST), which go to the ring slots of K(kb) and
@@ -378,11 +389,12 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   };
   for (int kb = 0; kb < nst; kb += 2) {
     int issued = issue(kb);
-    if (kb < w.wave_nkb) w.step(kb, pa, pb);
+    static_assert(G::NSTAGE == 2, "the loop alternates two ring stages");
+    if (kb < w.wave_nkb) w.template step<0>(kb, pa, pb);
     publish(issued);
     if (kb + 1 >= nst) break;
     issued = issue(kb + 1);
-    if (kb + 1 < w.wave_nkb) w.step(kb + 1, pb, pa);
+    if (kb + 1 < w.wave_nkb) w.template step<1>(kb + 1, pb, pa);
     publish(issued);
   }
 

@@ -203,6 +203,36 @@ struct Phase {
     }
   }
 
+  // The score MFMAs with the lane's K operand offsets precomputed: ko[ks] is
+  // the byte offset, within a 64-key tile, of this lane's 16-byte chunk of
+  // feature slice ks (row li, swizzled); rows 32jt + li add 32jt rows.  The
+  // empty asm makes each offset opaque, so that the compiler keeps the sums
+  // in registers instead of re-adding their two parts in every block.
+  static constexpr int NKO = BF16 ? D / 16 : D / 8;
+  MHA_INLINE void k_offsets(uint32_t (&ko)[NKO], int li, int hi) {
+    const int sw = S::k(li);
+#pragma unroll
+    for (int ks = 0; ks < NKO; ++ks) {
+      ko[ks] = (uint32_t)(li * ROWB + ((BF16 ? (2 * ks + hi) : (ks + (D / 8) * hi)) ^ sw) * 16);
+      asm volatile("" : "+v"(ko[ks]));
+    }
+  }
+  MHA_INLINE void scores_ko(f32x16 (&s)[NS], const char* kt, const u32x4 (&qf)[NQF],
+                            const uint32_t (&ko)[NKO]) {
+    static_assert(BF16, "precomputed K offsets: bf16 tiles");
+#pragma unroll
+    for (int jt = 0; jt < NS; ++jt) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + jt * 32 * ROWB + ko[ks]);
+        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), s[jt], 0, 0, 0);
+      }
+    }
+  }
+
   // Schedule of the score MFMAs: keep the K operand reads four MFMAs ahead
   // of their use (the compiler's own schedule issues them about two ahead,
   // which leaves the MFMAs waiting on LDS latency).
