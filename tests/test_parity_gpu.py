@@ -329,3 +329,24 @@ def test_errors_through_binding(gpu):
     with pytest.raises(mha.MhaError) as e:
         mha.forward(q96, q96.clone(), q96.clone())
     assert e.value.status == 4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_take_the_exact_path(gpu, causal):
+    # Scores that climb by far more than the on-demand check allows from one
+    # 64-key block to the next: key j is 2j along the query's direction, so
+    # a block's scores beat the previous block's by about 23 in log2 units
+    # (scale 1/8).  Every block then takes the exact path (block max, raise,
+    # rescale); the result must still match the oracle.
+    B, H, n, d = 1, 2, 320, 64
+    _, _, v, _ = inputs.draw(B, H, n, n, d, d, "bf16", seed=61)
+    q = torch.zeros(B, H, n, d)
+    k = torch.zeros(B, H, n, d)
+    q[..., 0] = 1.0
+    k[..., 0] = 2.0 * torch.arange(n, dtype=torch.float32)
+    k[..., 1] = torch.linspace(-1, 1, n)          # a little structure off the ramp
+    q[..., 1] = torch.linspace(1, -1, n)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o = run_gpu(q, k, v, causal=causal)
+    ref = oracle.attention(q, k, v, causal=causal)
+    compare(o, ref, TOL["bf16"], "rising scores")
