@@ -52,10 +52,10 @@
 extern "C" {
 #endif
 
-#define MHA_ABI_VERSION 4
+#define MHA_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
-enum {
+typedef enum mha_status {
     MHA_OK = 0,
     MHA_ERR_NULL = 1,        /* a required pointer is NULL */
     MHA_ERR_SHAPE = 2,       /* negative size, or causal with n != m */
@@ -67,7 +67,7 @@ enum {
     MHA_ERR_ALIGN = 8,       /* a tensor pointer is not 16-byte aligned (lse, slopes: 4) */
     MHA_ERR_MODE = 9,        /* mask_mode is not one of the MHA_MASK_* values */
     MHA_ERR_WORKSPACE = 10   /* decode workspace missing, too small, misaligned or overlapping */
-};
+} mha_status;
 
 /* Mask modes of the extended entry points (key padding always applies). */
 enum {
@@ -76,14 +76,14 @@ enum {
     MHA_MASK_CAUSAL_BOTTOM_RIGHT = 2 /* query i is the token at position i + L_b - n */
 };
 
-/* Element types. */
-enum { MHA_F32 = 0, MHA_BF16 = 1 };
+/* Element type of every tensor argument of one call. */
+typedef enum mha_dtype { MHA_F32 = 0, MHA_BF16 = 1 } mha_dtype;
 
 /* MHA_ABI_VERSION of the loaded library. */
 int mha_abi_version(void);
 
 /* A static, human-readable string for a status code (never NULL). */
-const char *mha_status_string(int status);
+const char *mha_status_string(mha_status status);
 
 /*
  * Host-side argument check of mha_forward, without any HIP call.
@@ -101,10 +101,10 @@ const char *mha_status_string(int status);
  *
  * Returns MHA_OK or the first error found.
  */
-int mha_validate(const void *Q, const void *K, const void *V,
-                 const int32_t *key_lens, int causal, float scale,
-                 const void *O, int64_t B, int64_t H, int64_t n, int64_t m,
-                 int64_t d_k, int64_t d_v, int dtype);
+mha_status mha_validate(const void *Q, const void *K, const void *V,
+                        const int32_t *key_lens, int causal, float scale,
+                        const void *O, int64_t B, int64_t H, int64_t n, int64_t m,
+                        int64_t d_k, int64_t d_v, mha_dtype dtype);
 
 /*
  * Enqueue the attention forward pass on `stream` (a hipStream_t; NULL is the
@@ -112,10 +112,10 @@ int mha_validate(const void *Q, const void *K, const void *V,
  * When B, H or n is 0 there is nothing to write and nothing is enqueued;
  * m == 0 writes zeros to O.  Returns MHA_OK once the kernel is enqueued.
  */
-int mha_forward(const void *Q, const void *K, const void *V,
-                const int32_t *key_lens, int causal, float scale, void *O,
-                int64_t B, int64_t H, int64_t n, int64_t m,
-                int64_t d_k, int64_t d_v, int dtype, void *stream);
+mha_status mha_forward(const void *Q, const void *K, const void *V,
+                       const int32_t *key_lens, int causal, float scale, void *O,
+                       int64_t B, int64_t H, int64_t n, int64_t m,
+                       int64_t d_k, int64_t d_v, mha_dtype dtype, void *stream);
 
 /*
  * ---- Extended forward pass -------------------------------------------------
@@ -151,17 +151,31 @@ int mha_forward(const void *Q, const void *K, const void *V,
  * MHA_ERR_MODE, lse overlapping any other argument MHA_ERR_ALIAS.  Slopes
  * are device data and are not validated.
  */
-int mha_validate_ex(const void *Q, const void *K, const void *V,
-                    const int32_t *key_lens, int mask_mode,
-                    const float *alibi_slopes, float scale, const void *O,
-                    const float *lse, int64_t B, int64_t H, int64_t H_kv,
-                    int64_t n, int64_t m, int64_t d_k, int64_t d_v, int dtype);
+mha_status mha_validate_ex(const void *Q, const void *K, const void *V,
+                           const int32_t *key_lens, int mask_mode,
+                           const float *alibi_slopes, float scale, const void *O,
+                           const float *lse, int64_t B, int64_t H, int64_t H_kv,
+                           int64_t n, int64_t m, int64_t d_k, int64_t d_v, mha_dtype dtype);
 
-int mha_forward_ex(const void *Q, const void *K, const void *V,
-                   const int32_t *key_lens, int mask_mode,
-                   const float *alibi_slopes, float scale, void *O, float *lse,
-                   int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
-                   int64_t d_k, int64_t d_v, int dtype, void *stream);
+mha_status mha_forward_ex(const void *Q, const void *K, const void *V,
+                          const int32_t *key_lens, int mask_mode,
+                          const float *alibi_slopes, float scale, void *O, float *lse,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                          int64_t d_k, int64_t d_v, mha_dtype dtype, void *stream);
+
+/*
+ * The forward kernel instance that mha_forward / mha_forward_ex launch for
+ * these sizes, as profilers name it (e.g.
+ * "mha::attn_fwd_kernel<__bf16, 128, 8, 1, true, false>": element type,
+ * head width, waves per workgroup, key groups per workgroup, causal, ALiBi),
+ * so that a kernel trace can be matched to a call.  mask_mode as for
+ * mha_forward_ex (mha_forward's causal flag is MHA_MASK_CAUSAL); alibi: 0
+ * or 1.  Pure host arithmetic; returns a static string, or NULL for
+ * arguments mha_forward_ex would refuse on their sizes, dtype or mode.
+ */
+const char *mha_forward_kernel_name(int64_t B, int64_t H, int64_t H_kv,
+                                    int64_t n, int64_t m, int64_t d,
+                                    mha_dtype dtype, int mask_mode, int alibi);
 
 /*
  * ---- Attention weights --------------------------------------------------------
@@ -178,17 +192,17 @@ int mha_forward_ex(const void *Q, const void *K, const void *V,
  * {64, 128}; one head's A must stay under 2 GiB.  Errors as for
  * mha_forward_ex.
  */
-int mha_validate_weights(const void *Q, const void *K, const int32_t *key_lens,
-                         int mask_mode, const float *alibi_slopes, float scale,
-                         const float *lse, const void *A, int64_t B, int64_t H,
-                         int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
-                         int dtype);
+mha_status mha_validate_weights(const void *Q, const void *K, const int32_t *key_lens,
+                                int mask_mode, const float *alibi_slopes, float scale,
+                                const float *lse, const void *A, int64_t B, int64_t H,
+                                int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                                mha_dtype dtype);
 
-int mha_attention_weights(const void *Q, const void *K, const int32_t *key_lens,
-                          int mask_mode, const float *alibi_slopes, float scale,
-                          const float *lse, void *A, int64_t B, int64_t H,
-                          int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
-                          int dtype, void *stream);
+mha_status mha_attention_weights(const void *Q, const void *K, const int32_t *key_lens,
+                                 int mask_mode, const float *alibi_slopes, float scale,
+                                 const float *lse, void *A, int64_t B, int64_t H,
+                                 int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                                 mha_dtype dtype, void *stream);
 
 /*
  * ---- Decoding against a key/value cache ---------------------------------------
@@ -219,21 +233,21 @@ int mha_attention_weights(const void *Q, const void *K, const int32_t *key_lens,
  * at once need two workspaces.  Errors as for mha_forward_ex, and
  * MHA_ERR_WORKSPACE.
  */
-int mha_decode_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t n,
-                              int64_t m, int64_t d, int dtype, int64_t *bytes);
+mha_status mha_decode_workspace_size(int64_t B, int64_t H, int64_t H_kv, int64_t n,
+                                     int64_t m, int64_t d, mha_dtype dtype, int64_t *bytes);
 
-int mha_validate_decode(const void *Q, const void *K, const void *V,
-                        const int32_t *cache_lens, const float *alibi_slopes,
-                        float scale, const void *O, const float *lse,
-                        const void *workspace, int64_t workspace_bytes,
-                        int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
-                        int64_t d_k, int64_t d_v, int dtype);
+mha_status mha_validate_decode(const void *Q, const void *K, const void *V,
+                               const int32_t *cache_lens, const float *alibi_slopes,
+                               float scale, const void *O, const float *lse,
+                               const void *workspace, int64_t workspace_bytes,
+                               int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                               int64_t d_k, int64_t d_v, mha_dtype dtype);
 
-int mha_decode(const void *Q, const void *K, const void *V,
-               const int32_t *cache_lens, const float *alibi_slopes, float scale,
-               void *O, float *lse, void *workspace, int64_t workspace_bytes,
-               int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
-               int64_t d_k, int64_t d_v, int dtype, void *stream);
+mha_status mha_decode(const void *Q, const void *K, const void *V,
+                      const int32_t *cache_lens, const float *alibi_slopes, float scale,
+                      void *O, float *lse, void *workspace, int64_t workspace_bytes,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
+                      int64_t d_k, int64_t d_v, mha_dtype dtype, void *stream);
 
 /*
  * ---- Multi-head attention with its projections ---------------------------------
@@ -266,19 +280,30 @@ int mha_decode(const void *Q, const void *K, const void *V,
  * mha_forward_ex, plus MHA_ERR_WORKSPACE; sizes whose tensors pass 2 GiB are
  * MHA_ERR_UNSUPPORTED.  Enqueues four to five kernels on `stream`.
  */
-int mha_multihead_workspace_size(int64_t B, int64_t n, int64_t m,
-                                 int64_t d_model, int64_t H, int dtype,
-                                 int need_weights, int64_t *bytes);
+mha_status mha_multihead_workspace_size(int64_t B, int64_t n, int64_t m,
+                                        int64_t d_model, int64_t H, mha_dtype dtype,
+                                        int need_weights, int64_t *bytes);
 
-int mha_multihead_forward(const void *Xq, const void *Xk, const void *Xv,
-                          const void *Wq, const void *bq, const void *Wk,
-                          const void *bk, const void *Wv, const void *bv,
-                          const void *Wo, const void *bo,
-                          const int32_t *key_lens, int mask_mode, float scale,
-                          void *Y, void *A, void *workspace,
-                          int64_t workspace_bytes, int64_t B, int64_t n,
-                          int64_t m, int64_t d_model, int64_t H, int dtype,
-                          void *stream);
+/* Host-side argument check of mha_multihead_forward (no HIP call); the
+ * arguments are those of the call below without the stream. */
+mha_status mha_validate_multihead(const void *Xq, const void *Xk, const void *Xv,
+                                  const void *Wq, const void *bq, const void *Wk,
+                                  const void *bk, const void *Wv, const void *bv,
+                                  const void *Wo, const void *bo,
+                                  const int32_t *key_lens, int mask_mode, float scale,
+                                  const void *Y, const void *A, const void *workspace,
+                                  int64_t workspace_bytes, int64_t B, int64_t n,
+                                  int64_t m, int64_t d_model, int64_t H, mha_dtype dtype);
+
+mha_status mha_multihead_forward(const void *Xq, const void *Xk, const void *Xv,
+                                 const void *Wq, const void *bq, const void *Wk,
+                                 const void *bk, const void *Wv, const void *bv,
+                                 const void *Wo, const void *bo,
+                                 const int32_t *key_lens, int mask_mode, float scale,
+                                 void *Y, void *A, void *workspace,
+                                 int64_t workspace_bytes, int64_t B, int64_t n,
+                                 int64_t m, int64_t d_model, int64_t H, mha_dtype dtype,
+                                 void *stream);
 
 #ifdef __cplusplus
 }

@@ -24,10 +24,11 @@ def test_exports_every_declared_function(lib):
                           "mha_forward", "mha_validate_ex", "mha_forward_ex",
                           "mha_validate_weights", "mha_attention_weights",
                           "mha_decode_workspace_size", "mha_validate_decode", "mha_decode",
-                          "mha_multihead_workspace_size", "mha_multihead_forward"}
+                          "mha_multihead_workspace_size", "mha_multihead_forward",
+                          "mha_forward_kernel_name", "mha_validate_multihead"}
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mha_abi_version() == 4
+    assert lib.mha_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -333,3 +334,25 @@ def test_multihead_rejects_on_host(lib):
     assert mh_call(lib, scale=-1.0) == SCALE
     assert mh_call(lib, H=5) == SHAPE
     assert mh_call(lib, B=0) == OK                   # nothing to do
+
+
+def test_forward_kernel_name_follows_the_variant_rule(lib):
+    """The instance a launch of these sizes takes, spelled as profilers print
+    it; None for arguments the forward pass refuses."""
+    def name(B, H, Hkv, n, m, d, dtype=BF16, mode=0, alibi=0):
+        r = lib.mha_forward_kernel_name(B, H, Hkv, n, m, d, dtype, mode, alibi)
+        return None if r is None else r.decode()
+    # the long causal workload: 64 query blocks of 256 rows x 16 heads
+    assert name(1, 16, 16, 16384, 16384, 128, mode=1) == \
+        "mha::attn_fwd_kernel<__bf16, 128, 8, 1, true, false>"
+    # n = 128, d = 64: four-wave workgroups; one per 128 rows
+    assert name(32, 8, 8, 128, 128, 64) == "mha::attn_fwd_kernel<__bf16, 64, 4, 1, false, false>"
+    # few query blocks and a long key axis: two key groups
+    assert name(8, 16, 16, 256, 1024, 64) == "mha::attn_fwd_kernel<__bf16, 64, 8, 2, false, false>"
+    assert name(1, 8, 8, 16, 16, 64, dtype=F32) == \
+        "mha::attn_fwd_kernel<float, 64, 4, 1, false, false>"
+    assert name(2, 8, 2, 4096, 4096, 128, mode=2, alibi=1).endswith("true, true>")
+    assert name(1, 8, 8, 16, 16, 96) is None
+    assert name(1, 8, 3, 16, 16, 64) is None
+    assert name(1, 8, 8, 16, 16, 64, dtype=7) is None
+    assert name(1, 8, 8, 16, 16, 64, mode=3) is None

@@ -89,6 +89,11 @@ def load():
     lib.mha_multihead_forward.argtypes = [vp] * 11 + [vp, i32, fl, vp, vp, vp, i64,
                                                       i64, i64, i64, i64, i64, i32, vp]
     lib.mha_multihead_forward.restype = i32
+    lib.mha_validate_multihead.argtypes = [vp] * 11 + [vp, i32, fl, vp, vp, vp, i64,
+                                                       i64, i64, i64, i64, i64, i32]
+    lib.mha_validate_multihead.restype = i32
+    lib.mha_forward_kernel_name.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32]
+    lib.mha_forward_kernel_name.restype = ctypes.c_char_p
     _lib = lib
     return lib
 
@@ -97,7 +102,7 @@ def header_functions():
     """Names of the functions include/libmha.h declares."""
     with open(HEADER_PATH, encoding="utf-8") as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(mha_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|mha_status|const char \*)\s*(mha_\w+)\s*\(", text, re.M)))
 
 
 def abi_version() -> int:

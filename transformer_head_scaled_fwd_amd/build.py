@@ -20,6 +20,9 @@ LIB = os.path.join(PKG, "libmha.so")
 
 SOURCES = ["mha_abi.hip", "mha_fwd_kernel.hip", "mha_weights_kernel.hip",
            "mha_decode_kernel.hip", "mha_proj_kernel.hip"]
+# Host-only C++ (argument checks, plans): built with g++, no HIP header.
+HOST_SOURCES = ["mha_host.cpp"]
+GXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 OBJDIR = os.path.join(PKG, "_build")
 
 HIPCC_FLAGS = [
@@ -35,6 +38,11 @@ def hipcc() -> str:
 
 def compile_command(src: str, obj: str):
     return ([hipcc()] + [f for f in HIPCC_FLAGS if f != "-shared"]
+            + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+
+
+def host_compile_command(src: str, obj: str, extra=()):
+    return (["g++"] + GXX_FLAGS + list(extra)
             + ["-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
 
 
@@ -61,9 +69,13 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     tag = "%d" % os.getpid()
     objs = [os.path.join(OBJDIR, s.replace(".hip", ".%s.o" % tag)) for s in SOURCES]
+    hobjs = [os.path.join(OBJDIR, s.replace(".cpp", ".%s.o" % tag)) for s in HOST_SOURCES]
+    cmds = [compile_command(s, o) for s, o in zip(SOURCES, objs)]
+    cmds += [host_compile_command(s, o) for s, o in zip(HOST_SOURCES, hobjs)]
+    objs = objs + hobjs
     try:
-        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-            list(ex.map(lambda so: _run(compile_command(*so), verbose), zip(SOURCES, objs)))
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            list(ex.map(lambda c: _run(c, verbose), cmds))
         tmp = LIB + ".tmp" + tag
         _run(link_command(objs, tmp), verbose)
     finally:

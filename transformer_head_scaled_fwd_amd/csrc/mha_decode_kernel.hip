@@ -141,8 +141,12 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     G1::template wait_loads<LOADS>();
     f32x16 sc[NS];
     P::scores(sc, ktile, qf, li, hi);
-    // The K tile is free once the score MFMAs have their operands.
-    if (more) G1::template stage<true>(kt_lds, kbase, kv_bytes, kb + NW, 0, lane);
+    // The K tile is free once the score MFMAs have their operands: wait for
+    // this wave's LDS reads before the direct loads overwrite the tile.
+    if (more) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      G1::template stage<true>(kt_lds, kbase, kv_bytes, kb + NW, 0, lane);
+    }
     if constexpr (ALIBI) P::bias(sc, (float)(prow - kb * BC - 4 * hi), sr);
     if (kb * BC + BC > lim_min) P::mask(sc, row_lim - kb * BC - 4 * hi);
     // Online softmax, not thresholded here: one block per step is cheap.
@@ -161,7 +165,10 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     if (more) G1::template wait_loads<LOADS>();
     else G1::template wait_loads<0>();
     P::pv(o, vtile, pf, lane);
-    if (more) G1::template stage<false>(vt_lds, vbase, kv_bytes, kb + NW, 0, lane);
+    if (more) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      G1::template stage<false>(vt_lds, vbase, kv_bytes, kb + NW, 0, lane);
+    }
   }
   G1::template wait_loads<0>();
 
@@ -289,34 +296,6 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
 template <typename T, int D>
 constexpr int dec_waves() {
   return (sizeof(T) == 4 && D == 128) ? 2 : 4;
-}
-
-DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int d,
-                       bool bf16) {
-  DecodePlan p;
-  const int nw = (!bf16 && d == 128) ? 2 : 4;
-  const int64_t R = (H / H_kv) * n;
-  p.nrs = (R + kRowsPerWave - 1) / kRowsPerWave;
-  const int64_t nkb = (m + BC - 1) / BC;
-  const int64_t units = B * H_kv * p.nrs;
-  // About one workgroup per CU of a 256-CU device (a workgroup's four K/V
-  // tile pairs take 128 KiB of the CU's 160 KiB of LDS, so one is resident at
-  // a time): each wave then streams several key blocks, the next block's
-  // loads overlapping the current block's compute, instead of one block per
-  // wave and several rounds of workgroups.  At least one key block per wave
-  // in every split.
-  const int64_t target = 256;
-  int64_t nsplit = units >= target ? 1 : (target + units - 1) / units;
-  const int64_t max_split = (nkb + nw - 1) / nw;
-  if (nsplit > max_split) nsplit = max_split;
-  if (nsplit < 1) nsplit = 1;
-  int64_t sb = (nkb + nsplit - 1) / nsplit;
-  sb = ((sb + nw - 1) / nw) * nw;
-  if (sb < nw) sb = nw;
-  p.split_blocks = sb;
-  p.nsplit = nkb > 0 ? (nkb + sb - 1) / sb : 1;
-  p.workspace_bytes = p.nsplit > 1 ? B * H * n * p.nsplit * ((int64_t)d + 2) * 4 : 0;
-  return p;
 }
 
 template <typename T, int D, bool ALIBI>

@@ -547,27 +547,15 @@ static hipError_t launch_variant(const LaunchArgs& a) {
   return causal ? launch_one<T, D, NW, KS, true, false>(a) : launch_one<T, D, NW, KS, false, false>(a);
 }
 
-// Workgroup shape:
-//  - 8 waves as 8 row groups (256 query rows, one workgroup per CU) for bf16
-//    with d = 128 when the query axis gives every CU several workgroups;
-//  - 8 waves as 4 row groups x 2 key groups (128 rows) for bf16 when 128-row
-//    workgroups would leave one wave per SIMD (at most one workgroup per CU)
-//    and the key axis is long (m >= 1024): one wave would walk all of it
-//    serially, and splitting the walk halves the chain of dependent blocks.
-//    The merge at the end costs about as much as three blocks of the walk,
-//    so shorter walks keep one key group (measured: m = 256 and 512 lose
-//    4-11%, m = 1024, 2048 and 4096 gain 4%, 9% and 12%);
-//  - otherwise 4 waves (128 rows, two workgroups per CU).
+// Workgroup shape as forward_variant (mha_host.cpp) chooses it.
 template <typename T, int D>
 static hipError_t launch_d(const LaunchArgs& a) {
+  const FwdVariant v = forward_variant(sizeof(T) == 2, D, a.B, a.H, a.n, a.m);
   if constexpr (sizeof(T) == 2) {
-    if constexpr (D == 128) {
-      const int64_t big_blocks = ((a.n + 255) / 256) * a.B * a.H;
-      if (big_blocks >= 4 * 256 && big_blocks <= (int64_t)UINT32_MAX / 512)
-        return launch_variant<T, D, 8, 1>(a);
+    if (v.nw == 8 && v.ks == 1) {
+      if constexpr (D == 128) return launch_variant<T, D, 8, 1>(a);
     }
-    const int64_t blocks = ((a.n + 127) / 128) * a.B * a.H;
-    if (blocks <= 256 && a.m >= 16 * BC) return launch_variant<T, D, 8, 2>(a);
+    if (v.nw == 8 && v.ks == 2) return launch_variant<T, D, 8, 2>(a);
   }
   return launch_variant<T, D, 4, 1>(a);
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mha_host.h"
+
 namespace mha {
 
 // Arguments after host validation; sizes fit the kernels' 32-bit offsets.
@@ -61,15 +63,6 @@ struct DecodeArgs {
   void* stream;
 };
 
-// How the key axis is cut: row sets of 32 query rows, splits of
-// split_blocks key blocks, and the workspace the splits need (0 when the
-// whole axis fits one workgroup per row set).
-struct DecodePlan {
-  int64_t nrs, nsplit, split_blocks, workspace_bytes;
-};
-
-DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int d,
-                       bool bf16);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p);
 
 // One projection C = A W^T + bias: A [M, K] (or, with a_heads, the
