@@ -30,7 +30,20 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
            "-std=c11", "-Wall", "-Wextra", _SRC, "-o", _LIB, "-lm"]
 
+# Sanitizer build of the same source (address and undefined-behaviour
+# checks), for running the pins under the sanitizers on the host.
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all"]
+
 _lib = None
+
+
+def build_sanitized(out: str) -> str:
+    """Compile the oracle with SAN_FLAGS into `out` (a shared object that
+    needs the sanitizer runtimes preloaded into the process that loads it)."""
+    cmd = [c for c in GCC_CMD[:-3] if c != "-O2"] + SAN_FLAGS + ["-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def build(force: bool = False) -> str:
@@ -48,8 +61,10 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        # MHA_ORACLE_LIB names another build of this source (the sanitizer
+        # build); otherwise the default build, compiled when stale.
+        path = os.environ.get("MHA_ORACLE_LIB") or build()
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
         lp = ctypes.POINTER(ctypes.c_int64)
@@ -249,26 +264,22 @@ def attention_ex_rows(q, k, v, rows, key_lens=None, causal=False,
     return out, lse
 
 
-def _linear(x, W, b):
-    """nn.Linear: x W^T + b, W [out, in] (a library matmul in fp64)."""
-    y = np.matmul(x, to_f64(W).T)
-    return y if b is None else y + to_f64(b)
-
-
 def multihead(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H, key_lens=None,
               causal=False, scale=None, return_weights=False):
-    """Multi-head attention around the core, as the pages write it
-    ("序列建模架构的演进与变革（二）" §4.9, "Transformer: 详解" §4.2,
-    "第2章：完整的 Transformer 架构" §2.2):
+    """The multi-head formula ("Transformer: 详解" §4.2, "第2章：完整的
+    Transformer 架构" §2.2; the projections carry a bias as the
+    nn.Linear layers of "序列建模架构的演进与变革（二）" §4.9 do):
 
-      Q = split_heads(xq Wq^T + bq),  K = split_heads(xk Wk^T + bk),
-      V = split_heads(xv Wv^T + bv)          [B, L, d_model] -> [B, H, L, d_k]
-      O = attention(Q, K, V, mask)           per head, the core oracle
-      Y = concat_heads(O) Wo^T + bo          [B, H, n, d_k] -> [B, n, d_model]
+      head_t = Attention(xq W_t^Q + b_t^Q, xk W_t^K + b_t^K, xv W_t^V + b_t^V)
+      Y      = Concat(head_1, ..., head_H) W^O + b^O
 
-    W* are [d_model, d_model] in nn.Linear's [out, in] layout, b* [d_model]
-    or None; d_k = d_model / H.  All fp64, no rounding of intermediates.
-    Returns Y, and with return_weights also A [B, H, n, m].
+    The weights come in nn.Linear's [out, in] layout, [d_model, d_model];
+    head t's projection W_t^Q is the transpose of rows t d_k .. (t+1) d_k of
+    Wq (and likewise for K and V), and the product of the concatenation with
+    W^O is the sum over heads of head_t times the transpose of columns
+    t d_k .. (t+1) d_k of Wo.  b* are [d_model] or None; d_k = d_model / H.
+    All fp64 with library matmuls, no rounding of intermediates.  Returns Y
+    [B, n, d_model], and with return_weights also A [B, H, n, m].
     """
     Xq, Xk, Xv = to_f64(xq), to_f64(xk), to_f64(xv)
     B, n, dm = Xq.shape
@@ -276,18 +287,25 @@ def multihead(xq, xk, xv, Wq, bq, Wk, bk, Wv, bv, Wo, bo, H, key_lens=None,
     if dm % H:
         raise ValueError("d_model must be a multiple of H")
     dk = dm // H
+    W = {name: to_f64(w) for name, w in (("q", Wq), ("k", Wk), ("v", Wv), ("o", Wo))}
+    bias = {name: (None if b is None else to_f64(b))
+            for name, b in (("q", bq), ("k", bk), ("v", bv), ("o", bo))}
 
-    def split(x, L):
-        return np.ascontiguousarray(x.reshape(B, L, H, dk).transpose(0, 2, 1, 3))
+    def head_projection(x, name, t):
+        """x W_t + b_t for head t: [B, L, d_model] -> [B, L, d_k]."""
+        rows = slice(t * dk, (t + 1) * dk)
+        y = np.matmul(x, W[name][rows].T)
+        return y if bias[name] is None else y + bias[name][rows]
 
-    Q = split(_linear(Xq, Wq, bq), n)
-    K = split(_linear(Xk, Wk, bk), m)
-    V = split(_linear(Xv, Wv, bv), m)
+    Q = np.stack([head_projection(Xq, "q", t) for t in range(H)], axis=1)  # [B, H, n, dk]
+    K = np.stack([head_projection(Xk, "k", t) for t in range(H)], axis=1)
+    V = np.stack([head_projection(Xv, "v", t) for t in range(H)], axis=1)
     res = attention_ex(Q, K, V, key_lens=key_lens, causal=causal, scale=scale,
                        return_weights=return_weights)
     O = res[0] if return_weights else res
-    concat = O.transpose(0, 2, 1, 3).reshape(B, n, dm)
-    Y = _linear(concat, Wo, bo)
+    Y = np.zeros((B, n, dm)) if bias["o"] is None else np.broadcast_to(bias["o"], (B, n, dm)).copy()
+    for t in range(H):
+        Y += np.matmul(O[:, t], W["o"][:, t * dk:(t + 1) * dk].T)
     return (Y, res[2]) if return_weights else Y
 
 
@@ -297,7 +315,7 @@ def threads() -> int:
 
 
 def library_path() -> str:
-    return _LIB
+    return os.environ.get("MHA_ORACLE_LIB") or _LIB
 
 
 __all__ = ["attention", "attention_rows", "attention_ex", "attention_ex_rows", "multihead",

@@ -88,14 +88,17 @@ def test_multihead_zero_query_projection_is_mean_pooling():
 
 
 MHA_MUTANTS = {
-    "heads_split_before_tokens": ("x.reshape(B, L, H, dk).transpose(0, 2, 1, 3)",
-                                  "x.reshape(B, H, L, dk)"),
-    "concat_without_transpose": ("O.transpose(0, 2, 1, 3).reshape(B, n, dm)",
-                                 "O.reshape(B, n, dm)"),
-    "key_projection_on_values": ("K = split(_linear(Xk, Wk, bk), m)",
-                                 "K = split(_linear(Xv, Wk, bk), m)"),
-    "weight_not_transposed": ("np.matmul(x, to_f64(W).T)", "np.matmul(x, to_f64(W))"),
-    "output_bias_dropped": ("Y = _linear(concat, Wo, bo)", "Y = _linear(concat, Wo, None)"),
+    # heads taken as every H-th feature instead of contiguous blocks of d_k
+    "heads_interleaved": ("rows = slice(t * dk, (t + 1) * dk)", "rows = slice(t, dm, H)"),
+    # the projection uses columns of the [out, in] weight (its transpose)
+    "projection_transposed": ("np.matmul(x, W[name][rows].T)", "np.matmul(x, W[name][:, rows])"),
+    "key_projection_on_values": ('K = np.stack([head_projection(Xk, "k", t)',
+                                 'K = np.stack([head_projection(Xv, "k", t)'),
+    # head t meets rows, not columns, of the output weight
+    "output_projection_transposed": ('W["o"][:, t * dk:(t + 1) * dk].T',
+                                     'W["o"][t * dk:(t + 1) * dk, :]'),
+    "output_bias_dropped": ('Y = np.zeros((B, n, dm)) if bias["o"] is None else',
+                            'Y = np.zeros((B, n, dm)) if True else'),
 }
 
 
@@ -103,7 +106,7 @@ MHA_MUTANTS = {
 def test_mha_pins_catch_planted_mistake(monkeypatch, name):
     import inspect
     old, new = MHA_MUTANTS[name]
-    src = inspect.getsource(oracle._linear) + "\n" + inspect.getsource(oracle.multihead)
+    src = inspect.getsource(oracle.multihead)
     assert old in src
     ns = dict(oracle.__dict__)
     exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
