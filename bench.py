@@ -109,9 +109,31 @@ def upload(torch, w, seed_offset=0):
     return (q.to(dev), k.to(dev), v.to(dev), kld, kl), (q, k, v, kl)
 
 
-def time_launches(torch, mha, sets, w, steps, warmup):
-    """Warmup, then `steps` launches cycling over `sets`; per-launch event
-    pairs and one pair around the whole region, all on the launch stream."""
+def prewarm(torch, launch, stream, ms, max_launches=4000):
+    """Untimed launches until `ms` milliseconds of GPU time have passed (or
+    max_launches): the device raises its clocks over the first tens of
+    milliseconds of sustained work, so a short warmup alone leaves the
+    timed launches on the ramp.  Returns (GPU ms spent, launches)."""
+    spent, count, batch = 0.0, 0, 4
+    while spent < ms and count < max_launches:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            launch(count)
+            count += 1
+        e1.record(stream)
+        e1.synchronize()
+        spent += e0.elapsed_time(e1)
+        batch = min(2 * batch, 64)
+    return spent, count
+
+
+def time_launches(torch, mha, sets, w, steps, warmup, prewarm_ms=0.0):
+    """A time-based pre-warm (prewarm_ms of GPU time), `warmup` untimed
+    launches, then `steps` launches cycling over `sets`; per-launch event
+    pairs and one pair around the whole region, all on the launch stream.
+    Returns (region ms, per-launch ms, first output, (prewarm ms, launches))."""
     stream = torch.cuda.current_stream()
     outs = [torch.empty((w.B, w.H, w.n, w.d), dtype=s[0].dtype, device="cuda:0") for s in sets]
 
@@ -120,6 +142,7 @@ def time_launches(torch, mha, sets, w, steps, warmup):
         mha.forward(q, k, v, key_lens=kl, causal=w.causal, scale=w.scale,
                     out=outs[i % len(sets)], stream=stream.cuda_stream)
 
+    pw = prewarm(torch, launch, stream, prewarm_ms) if prewarm_ms > 0 else (0.0, 0)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -136,7 +159,7 @@ def time_launches(torch, mha, sets, w, steps, warmup):
     t1.record(stream)
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
-    return t0.elapsed_time(t1), per, outs[0]
+    return t0.elapsed_time(t1), per, outs[0], pw
 
 
 def time_graph(torch, mha, sets, w, launches=64, replays=5):
@@ -217,7 +240,7 @@ def time_copy_floor(torch, nbytes, launches=64, replays=5, rotate_bytes=1 << 30)
     return best
 
 
-def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=0.0):
     from transformer_head_scaled_fwd_amd import inputs
     w = inputs.WORKLOADS[name]
     first, host = upload(torch, w)
@@ -230,7 +253,7 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     for s in range(1, nsets):
         q, k, v = (torch.roll(t, shifts=s, dims=0).contiguous() + 0 for t in first[:3])
         sets.append((q, k, v, first[3], first[4]))
-    total_ms, per, out0 = time_launches(torch, mha, sets, w, steps, warmup)
+    total_ms, per, out0, pw = time_launches(torch, mha, sets, w, steps, warmup, prewarm_ms)
     out0 = out0.cpu()  # the output of the first input set, the host inputs
     graph_us = time_graph(torch, mha, sets, w) if w.metric_flops() < 1e11 else None
     kl = first[4]
@@ -241,8 +264,13 @@ def bench_workload(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     avg = total_ms / steps
     kern = statistics.mean(per)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    kname = mha.load().mha_forward_kernel_name(w.B, w.H, w.H, w.n, w.m, w.d,
+                                               mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32,
+                                               1 if w.causal else 0, 0)
     return {
-        "workload": name, "dtype": w.dtype, "seed": w.seed, "B": w.B, "H": w.H, "n": w.n, "m": w.m,
+        "workload": name, "kernel": kname.decode() if kname else None,
+        "prewarm_ms": pw[0], "prewarm_launches": pw[1],
+        "dtype": w.dtype, "seed": w.seed, "B": w.B, "H": w.H, "n": w.n, "m": w.m,
         "d": w.d, "causal": w.causal, "key_lens": None if w.lens is None else list(w.lens),
         "input_sets": len(sets), "launches": steps,
         "ms_per_launch": avg, "kernel_ms_mean": kern, "kernel_ms_median": statistics.median(per),
@@ -440,42 +468,58 @@ def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     }
 
 
-def cpu_baseline(w, host, budget_s):
-    """The oracle as it stands, on a bounded sample of query rows of the
-    headline workload, timed on this host's cores."""
+def cpu_baseline(w, host, max_s):
+    """The oracle as it stands, timed on this host's cores over the whole
+    headline workload (every query row of every head), its result kept for
+    the parity check.  A probe on 64 rows first estimates the full run; only
+    if that estimate exceeds max_s seconds does it fall back to distinct
+    rows drawn without replacement, as many as fit in max_s / 4."""
     import oracle
     q, k, v, kl = host
     Q, K, V = oracle.to_f64(q), oracle.to_f64(k), oracle.to_f64(v)
+    total_rows = w.B * w.H * w.n
     rng = np.random.Generator(np.random.PCG64(2024))
 
-    def sample(r):
-        b = rng.integers(0, w.B, r)
-        t = rng.integers(0, w.H, r)
-        i = rng.integers(0, w.n, r)
+    def rows_of(flat):
+        flat = np.sort(flat)
+        b, rem = np.divmod(flat, w.H * w.n)
+        t, i = np.divmod(rem, w.n)
         return np.stack([b, t, i], 1).astype(np.int64)
 
     def work(rows):
         keys = rows[:, 2] + 1 if w.causal else np.full(len(rows), w.m)
         if kl is not None:
             keys = np.minimum(keys, np.asarray(kl)[rows[:, 0]])
-        return 4.0 * w.d * float(keys.sum())
+        return 4.0 * w.d * float(np.maximum(keys, 0).sum())
 
-    probe = sample(64)
+    probe = rows_of(rng.choice(total_rows, size=min(64, total_rows), replace=False))
     t = time.perf_counter()
     oracle.attention_rows(Q, K, V, probe, key_lens=kl, causal=w.causal, scale=w.scale)
     dt = max(time.perf_counter() - t, 1e-3)
     rate = work(probe) / dt
-    target = max(64, int(len(probe) * budget_s / dt))
-    rows = sample(min(target, 200000))
-    t = time.perf_counter()
-    ref = oracle.attention_rows(Q, K, V, rows, key_lens=kl, causal=w.causal, scale=w.scale)
-    dt = time.perf_counter() - t
-    f = work(rows)
+    all_rows = rows_of(np.arange(total_rows))
+    full_work = work(all_rows)
+    if full_work / rate <= max_s:
+        t = time.perf_counter()
+        ref = oracle.attention(Q, K, V, key_lens=kl, causal=w.causal, scale=w.scale)
+        dt = time.perf_counter() - t
+        rows, f = None, full_work
+        sample = ("all %d query rows of the %d heads of %s (the whole workload); useful FLOPs "
+                  "4*d*(valid keys) per row; fp64 on the host cores" % (total_rows, w.B * w.H, w.name))
+    else:
+        target = int(total_rows * (max_s / 4.0) / (full_work / rate))
+        rows = rows_of(rng.choice(total_rows, size=max(64, min(target, total_rows)),
+                                  replace=False))
+        t = time.perf_counter()
+        ref = oracle.attention_rows(Q, K, V, rows, key_lens=kl, causal=w.causal, scale=w.scale)
+        dt = time.perf_counter() - t
+        f = work(rows)
+        sample = ("%d distinct query rows drawn without replacement (seeded) from the %d of %s; "
+                  "useful FLOPs 4*d*(valid keys) per row; fp64 on the host cores"
+                  % (len(rows), total_rows, w.name))
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle", "seconds": dt, "probe_rate_tflops": rate / 1e12,
-            "sample": "%d query rows drawn uniformly (seeded) from the %d heads of %s; "
-                      "useful FLOPs 4*d*(valid keys) per row; fp64 on the host cores"
-                      % (len(rows), w.B * w.H, w.name)}, rows, ref, dt
+            "sample": sample}, rows, ref, dt
 
 
 TOL = {"f32": 1e-5, "bf16": 1.5e-2}
@@ -494,14 +538,16 @@ def cpu_model() -> str:
 
 def parity(w, host, out, rows=None, ref=None, oracle_s=None):
     """The oracle (timed on this host's cores) against the GPU output of the
-    same input bits: max-abs error over every element, or over the sampled
-    rows when `rows` is given (with the oracle's result `ref` for them)."""
+    same input bits: max-abs error over every element (the oracle's full
+    result `ref`, or a fresh oracle run when it is None), or over the
+    sampled rows `rows` with the oracle's result `ref` for them."""
     import oracle
     q, k, v, kl = host
     if ref is None:
         t = time.perf_counter()
         ref = oracle.attention(q, k, v, key_lens=kl, causal=w.causal, scale=w.scale)
         oracle_s = time.perf_counter() - t
+    if rows is None:
         got = oracle.to_f64(out)
         compared = "all %d outputs" % got.size
     else:
@@ -543,7 +589,11 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-max-seconds", type=float, default=150.0,
+                    help="longest oracle run the baseline takes on the whole headline workload "
+                         "before it samples rows instead")
+    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+                    help="GPU time of untimed headline launches before the warmup steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
@@ -565,7 +615,8 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     print("bench: %s steps=%d warmup=%d" % (w.name, args.steps, args.warmup),
           file=sys.stderr, flush=True)
-    head, host, _, head_out = bench_workload(torch, mha, w.name, args.steps, args.warmup)
+    head, host, _, head_out = bench_workload(torch, mha, w.name, args.steps, args.warmup,
+                                             prewarm_ms=args.prewarm_ms)
     others = []
     checks = []  # (workload, host inputs, GPU output) for the oracle comparison
     if not args.no_others:
@@ -592,7 +643,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu, rows, ref, dt = cpu_baseline(w, host, args.cpu_seconds)
+        cpu, rows, ref, dt = cpu_baseline(w, host, args.cpu_max_seconds)
         head["parity"] = parity(w, host, head_out, rows=rows, ref=ref, oracle_s=dt)
         for wk, o_host, o_out, res in checks:
             print("bench: oracle parity %s" % wk.name, file=sys.stderr, flush=True)
@@ -608,6 +659,7 @@ def main():
         "value": head["metric_flops"] / (head["ms_per_launch"] * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "prewarm_ms": head["prewarm_ms"], "prewarm_launches": head["prewarm_launches"],
         "ms_per_step": head["ms_per_launch"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
@@ -624,7 +676,7 @@ def main():
         "frac_copy_floor_n128": None if sec is None else sec["graph_frac_copy_floor"],
         "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "attn_fwd_kernel<bf16,%d,%s>" % (w.d, "causal" if w.causal else "full"),
+                     "kernel": head["kernel"],
                      "kernel_ms_mean": head["kernel_ms_mean"],
                      "kernel_ms_median": head["kernel_ms_median"],
                      "kernel_source_sha256_16": kernel_source_hash(),

@@ -74,3 +74,20 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_cpu_baseline_runs_the_whole_workload_or_distinct_rows():
+    import oracle
+    w = inputs.Workload("t", 2, 3, 40, 40, 64, "bf16", True, None, 3)
+    host = inputs.make(w)
+    cpu, rows, ref, dt = bench.cpu_baseline(w, host, max_s=1e6)
+    assert rows is None and "all 240 query rows" in cpu["sample"]
+    full = oracle.attention(*host[:3], key_lens=host[3], causal=True, scale=w.scale)
+    np.testing.assert_array_equal(ref, full)
+    # a budget no full run fits: distinct rows, the oracle's values for them
+    cpu, rows, ref, dt = bench.cpu_baseline(w, host, max_s=1e-9)
+    assert rows is not None and "without replacement" in cpu["sample"]
+    assert len({tuple(r) for r in rows}) == len(rows)
+    np.testing.assert_array_equal(ref, full[rows[:, 0], rows[:, 1], rows[:, 2]])
+    rec = bench.parity(w, host, host[0].new_zeros(host[0].shape), rows=rows, ref=ref)
+    assert rec["compared"] == "%d sampled rows" % len(rows)
