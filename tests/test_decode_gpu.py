@@ -83,6 +83,24 @@ def test_decode_ignores_workspace_contents_and_padding(gpu):
     assert torch.equal(o1, o3) and torch.equal(l1, l3)   # run to run
 
 
+def test_decode_workspace_reused_across_sizes(gpu):
+    # One workspace, filled with NaN first, serves calls of different sizes
+    # in turn, and every result matches the oracle.
+    cases = [(1, 32, 32, 1, 8192, 128, None), (2, 8, 1, 4, 5000, 64, (1000, 5000)),
+             (1, 32, 32, 1, 8192, 128, None), (3, 16, 4, 1, 2100, 128, (64, 2100))]
+    need = max(mha.decode_workspace_size(B, H, Hkv, n, m, d, mha.MHA_BF16)
+               for B, H, Hkv, n, m, d, _ in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws.view(torch.float32).fill_(float("nan"))
+    for i, (B, H, Hkv, n, m, d, lens) in enumerate(cases):
+        q, k, v, kl = draw(B, H, Hkv, n, m, d, "bf16", seed=1410 + i, lens=lens)
+        assert mha.decode_workspace_size(B, H, Hkv, n, m, d, mha.MHA_BF16) > 0
+        o, lse = run_decode(q, k, v, kl, None, workspace=ws)
+        o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal="bottom_right",
+                                             return_lse=True)
+        assert maxerr(o, o_ref, "O") <= TOL_O["bf16"]
+
+
 def test_decode_matches_forward_ex(gpu):
     # The same operation through the prefill-shaped kernel.
     B, H, Hkv, n, m, d = 2, 16, 4, 3, 1200, 64

@@ -350,3 +350,52 @@ def test_rising_scores_take_the_exact_path(gpu, causal):
     o = run_gpu(q, k, v, causal=causal)
     ref = oracle.attention(q, k, v, causal=causal)
     compare(o, ref, TOL["bf16"], "rising scores")
+
+
+def _variant(B, H, n, m, d, causal):
+    name = mha.load().mha_forward_kernel_name(B, H, H, n, m, d, mha.MHA_BF16, int(causal), 0)
+    return name.decode()
+
+
+def _ramp_inputs(B, H, n, m, d, step, seed):
+    # Key j lies `step * j` along the query's direction, so the scores of a
+    # 64-key block beat those of the block before by 64 * step * scale
+    # (about 33 in log2 units for step 4 at d = 128, 45 at d = 64): every
+    # block's weights against the running max pass the on-demand bound and
+    # the wave takes the exact path (block max, raise, rescale).
+    _, _, v, _ = inputs.draw(B, H, n, m, d, d, "bf16", seed=seed)
+    q = torch.zeros(B, H, n, d)
+    k = torch.zeros(B, H, m, d)
+    q[..., 0] = 1.0
+    k[..., 0] = step * torch.arange(m, dtype=torch.float32)
+    k[..., 1] = torch.linspace(-1, 1, m)
+    q[..., 1] = torch.linspace(1, -1, n)
+    return q.to(torch.bfloat16), k.to(torch.bfloat16), v
+
+
+@pytest.mark.parametrize("B,H,n,m,d,causal,variant", [
+    # eight waves over 256 query rows (the long-sequence workload's shape)
+    (16, 16, 1024, 1024, 128, True, "<__bf16, 128, 8, 1, true, false>"),
+    (16, 16, 1024, 1024, 128, False, "<__bf16, 128, 8, 1, false, false>"),
+    # two key groups per workgroup, merged at the end
+    (1, 4, 320, 1280, 128, False, "<__bf16, 128, 8, 2, false, false>"),
+    (1, 1, 1280, 1280, 64, True, "<__bf16, 64, 8, 2, true, false>"),
+])
+def test_rising_scores_take_the_exact_path_in_every_variant(gpu, B, H, n, m, d, causal, variant):
+    assert _variant(B, H, n, m, d, causal).endswith(variant)
+    q, k, v = _ramp_inputs(B, H, n, m, d, 4.0, seed=62)
+    o = run_gpu(q, k, v, causal=causal)
+    ref = oracle.attention(q, k, v, causal=causal)
+    compare(o, ref, TOL["bf16"], "rising scores, " + variant)
+
+
+def test_deterministic_eight_wave_d128(gpu):
+    # The eight-wave d = 128 variant that carries the long-sequence
+    # workload: bit-identical outputs run after run.
+    B, H, n, d = 16, 16, 1024, 128
+    assert _variant(B, H, n, n, d, True).endswith("<__bf16, 128, 8, 1, true, false>")
+    q, k, v, _ = inputs.draw(B, H, n, n, d, d, "bf16", seed=63, value_scale=0.5)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    outs = [mha.forward(qd, kd, vd, causal=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
