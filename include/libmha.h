@@ -250,6 +250,26 @@ mha_status mha_decode(const void *Q, const void *K, const void *V,
                       int64_t d_k, int64_t d_v, mha_dtype dtype, void *stream);
 
 /*
+ * mha_decode_noalloc: mha_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments without the workspace: when the key
+ * axis is split, the partial results go to a fixed scratch array of 8.5 MiB
+ * that the library keeps in device memory, one per GPU, until the process
+ * ends; the call allocates nothing.  Every size mha_decode accepts fits it
+ * (no split plan needs more); a plan that would not is MHA_ERR_UNSUPPORTED.
+ * All calls on one GPU share that GPU's array, and no call reads what an
+ * earlier one left there: calls that may overlap on one GPU (other streams
+ * or other host threads) race on it, and the caller must serialise them.
+ * Errors as for mha_decode; MHA_ERR_HIP also when the array's device
+ * address cannot be obtained.
+ */
+mha_status mha_decode_noalloc(const void *Q, const void *K, const void *V,
+                              const int32_t *cache_lens, const float *alibi_slopes,
+                              float scale, void *O, float *lse, int64_t B, int64_t H,
+                              int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                              int64_t d_v, mha_dtype dtype, void *stream);
+
+/*
  * ---- Multi-head attention with its projections ---------------------------------
  *
  * The layer around the core, as the pages write it ("序列建模架构的演进与变革

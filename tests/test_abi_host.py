@@ -25,7 +25,8 @@ def test_exports_every_declared_function(lib):
                           "mha_validate_weights", "mha_attention_weights",
                           "mha_decode_workspace_size", "mha_validate_decode", "mha_decode",
                           "mha_multihead_workspace_size", "mha_multihead_forward",
-                          "mha_forward_kernel_name", "mha_validate_multihead"}
+                          "mha_forward_kernel_name", "mha_validate_multihead",
+                          "mha_decode_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
     assert lib.mha_abi_version() == 5
@@ -356,3 +357,18 @@ def test_forward_kernel_name_follows_the_variant_rule(lib):
     assert name(1, 8, 3, 16, 16, 64) is None
     assert name(1, 8, 8, 16, 16, 64, dtype=7) is None
     assert name(1, 8, 8, 16, 16, 64, mode=3) is None
+
+
+def test_decode_noalloc_rejects_on_host(lib):
+    # Argument errors come back before any HIP call (no device here).
+    st = lib.mha_decode_noalloc(Q, K, V, None, None, 0.125, O, None, 8, 32, 5, 1, 16384,
+                                128, 128, BF16, None)
+    assert st == SHAPE
+    st = lib.mha_decode_noalloc(Q, K, V, None, None, 0.125, Q, None, 8, 32, 8, 1, 16384,
+                                128, 128, BF16, None)
+    assert st == ALIAS
+    st = lib.mha_decode_noalloc(Q, K, V, None, None, 0.125, O, None, 8, 32, 8, 1, 16384,
+                                96, 96, BF16, None)
+    assert st == UNSUP
+    assert lib.mha_decode_noalloc(None, None, None, None, None, 0.125, None, None, 0, 32, 8, 1,
+                                  16384, 128, 128, BF16, None) == OK

@@ -83,6 +83,9 @@ def load():
     lib.mha_decode.argtypes = [vp, vp, vp, vp, vp, fl, vp, vp, vp, i64,
                                i64, i64, i64, i64, i64, i64, i64, i32, vp]
     lib.mha_decode.restype = i32
+    lib.mha_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, fl, vp, vp,
+                                       i64, i64, i64, i64, i64, i64, i64, i32, vp]
+    lib.mha_decode_noalloc.restype = i32
     lib.mha_multihead_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32,
                                                  ctypes.POINTER(i64)]
     lib.mha_multihead_workspace_size.restype = i32

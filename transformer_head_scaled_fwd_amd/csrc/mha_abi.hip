@@ -93,15 +93,17 @@ mha_status mha_attention_weights(const void* Q, const void* K, const int32_t* ke
   return mha::launch_weights(a) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
 }
 
-mha_status mha_decode(const void* Q, const void* K, const void* V, const int32_t* cache_lens,
-               const float* alibi_slopes, float scale, void* O, float* lse, void* workspace,
-               int64_t workspace_bytes, int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
-               int64_t d_k, int64_t d_v, mha_dtype dtype, void* stream) {
-  const mha_status st = mha_validate_decode(Q, K, V, cache_lens, alibi_slopes, scale, O, lse, workspace,
-                                     workspace_bytes, B, H, H_kv, n, m, d_k, d_v, dtype);
-  if (st != MHA_OK) return st;
-  if (B == 0 || H == 0 || n == 0) return MHA_OK;
-  const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
+}  // extern "C"
+
+namespace {
+
+// The decode launch once the arguments have passed their check;
+// `workspace` is the caller's or the library's scratch.
+mha_status launch_decode_checked(const void* Q, const void* K, const void* V,
+                                 const int32_t* cache_lens, const float* alibi_slopes,
+                                 float scale, void* O, float* lse, void* workspace, int64_t B,
+                                 int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                                 mha_dtype dtype, const mha::DecodePlan& p, void* stream) {
   mha::DecodeArgs a;
   a.Q = Q;
   a.K = K;
@@ -122,6 +124,42 @@ mha_status mha_decode(const void* Q, const void* K, const void* V, const int32_t
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.stream = stream;
   return mha::launch_decode(a, p) == hipSuccess ? MHA_OK : MHA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mha_status mha_decode(const void* Q, const void* K, const void* V, const int32_t* cache_lens,
+                      const float* alibi_slopes, float scale, void* O, float* lse,
+                      void* workspace, int64_t workspace_bytes, int64_t B, int64_t H,
+                      int64_t H_kv, int64_t n, int64_t m, int64_t d_k, int64_t d_v,
+                      mha_dtype dtype, void* stream) {
+  const mha_status st = mha_validate_decode(Q, K, V, cache_lens, alibi_slopes, scale, O, lse,
+                                            workspace, workspace_bytes, B, H, H_kv, n, m, d_k,
+                                            d_v, dtype);
+  if (st != MHA_OK) return st;
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
+  return launch_decode_checked(Q, K, V, cache_lens, alibi_slopes, scale, O, lse, workspace, B, H,
+                               H_kv, n, m, d_k, dtype, p, stream);
+}
+
+mha_status mha_decode_noalloc(const void* Q, const void* K, const void* V,
+                              const int32_t* cache_lens, const float* alibi_slopes, float scale,
+                              void* O, float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t n,
+                              int64_t m, int64_t d_k, int64_t d_v, mha_dtype dtype,
+                              void* stream) {
+  const mha_status st = mha::check_decode_noalloc(Q, K, V, cache_lens, alibi_slopes, scale, O,
+                                                  lse, B, H, H_kv, n, m, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  if (B == 0 || H == 0 || n == 0) return MHA_OK;
+  const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16);
+  void* scratch = nullptr;
+  if (p.workspace_bytes > 0 && mha::decode_scratch_address(&scratch) != hipSuccess)
+    return MHA_ERR_HIP;
+  return launch_decode_checked(Q, K, V, cache_lens, alibi_slopes, scale, O, lse, scratch, B, H,
+                               H_kv, n, m, d_k, dtype, p, stream);
 }
 
 mha_status mha_multihead_forward(const void* Xq, const void* Xk, const void* Xv, const void* Wq,

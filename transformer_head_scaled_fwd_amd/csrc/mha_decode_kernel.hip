@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mha_launch.h"
 #include "mha_tiles.h"
 
@@ -339,6 +341,36 @@ static hipError_t launch_dec_d(const DecodeArgs& a, const DecodePlan& p) {
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p) {
   if (a.bf16) return a.d == 64 ? launch_dec_d<__bf16, 64>(a, p) : launch_dec_d<__bf16, 128>(a, p);
   return a.d == 64 ? launch_dec_d<float, 64>(a, p) : launch_dec_d<float, 128>(a, p);
+}
+
+// ---- the decode scratch of the allocation-free entry point ----
+//
+// A fixed array in device memory, one per GPU the library runs on, held
+// until the process ends, for callers that cannot allocate (code under HIP
+// graph capture, serving loops, harnesses that forbid allocation).  It
+// holds the split partial results in place of a caller's workspace.  The
+// array's name in host code is only a stand-in for the symbol: its device
+// address is taken once per device with hipGetSymbolAddress (with that
+// device current) and that address is what kernels receive.
+static __device__ __align__(256) char decode_scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch_address(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static void* addr[kMaxDevices] = {};
+  static std::mutex lock;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> guard(lock);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(decode_scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace mha

@@ -152,6 +152,22 @@ DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m,
   return p;
 }
 
+mha_status check_decode_noalloc(const void* Q, const void* K, const void* V,
+                                const int32_t* cache_lens, const float* alibi_slopes,
+                                float scale, const void* O, const float* lse, int64_t B,
+                                int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                                int64_t d_v, mha_dtype dtype) {
+  mha_status st = check_forward(Q, K, V, cache_lens, MHA_MASK_CAUSAL_BOTTOM_RIGHT, alibi_slopes,
+                                scale, O, lse, B, H, H_kv, n, m, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  st = check_decode_sizes(B, H, H_kv, n, m, d_k, dtype == MHA_BF16);
+  if (st != MHA_OK || B == 0 || H == 0 || n == 0) return st;
+  if (plan_decode(B, H, H_kv, n, m, (int)d_k, dtype == MHA_BF16).workspace_bytes >
+      kDecodeScratchBytes)
+    return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
 MhLayout mh_layout(int64_t B, int64_t n, int64_t m, int64_t d_model, int64_t H, int64_t es,
                    bool weights) {
   MhLayout l;

@@ -28,6 +28,21 @@ struct DecodePlan {
 DecodePlan plan_decode(int64_t B, int64_t H, int64_t H_kv, int64_t n, int64_t m, int d,
                        bool bf16);
 
+// Size of the library's own decode scratch (mha_decode_noalloc).  The key
+// axis is split only while fewer than 256 (batch, K/V head, row set) units
+// exist, each unit holds at most 32 query rows, and a unit gets at most
+// ceil(256 / units) splits, so every split plan needs at most
+// 32 * 510 * (128 + 2) * 4 = 8486400 bytes; 8.5 MiB covers it.
+constexpr int64_t kDecodeScratchBytes = (int64_t)17 << 19;
+
+// Argument check of mha_decode_noalloc: that of mha_decode without the
+// workspace, and the split plan must fit kDecodeScratchBytes.
+mha_status check_decode_noalloc(const void* Q, const void* K, const void* V,
+                                const int32_t* cache_lens, const float* alibi_slopes,
+                                float scale, const void* O, const float* lse, int64_t B,
+                                int64_t H, int64_t H_kv, int64_t n, int64_t m, int64_t d_k,
+                                int64_t d_v, mha_dtype dtype);
+
 // Workspace of the multi-head forward: Q, K, V, O in [B, H, L, d_k], then
 // the row log-sum-exp when the weights are requested; each part 256-byte
 // aligned.

@@ -65,6 +65,10 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p);
 
+// Device address, on the current device, of the decode scratch array of
+// kDecodeScratchBytes (looked up once per device).
+hipError_t decode_scratch_address(void** ptr);
+
 // One projection C = A W^T + bias: A [M, K] (or, with a_heads, the
 // concatenation of [B, H, L, dk] heads), W [N, K], C [M, N] (or, with
 // c_heads, split into [B, H, L, dk]); M = B * L.
