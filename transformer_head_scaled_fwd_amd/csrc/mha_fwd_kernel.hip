@@ -90,6 +90,7 @@ struct Walk {
   uint32_t ko[P::NKO]; // K operand offsets within a tile (bf16)
   f32x16 o[D / 32];    // O^T accumulator
   float m_run;         // running max of scale*log2(e)*s (per row)
+  float m_sub;         // what the weights subtract: m_run, or 0 while it is -inf
   float l_run;         // this lane's share of the row sum
 
   // gb: key block index (keys gb * BC onwards)
@@ -117,6 +118,7 @@ struct Walk {
     const float m_new = grew ? mx2 : m_run;
     const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
+    m_sub = (m_new == -__builtin_inff()) ? 0.0f : m_new;
     l_run *= alpha;
     return alpha;
   }
@@ -128,7 +130,7 @@ struct Walk {
         for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
     }
   }
-  MHA_MEMBER float msub() const { return (m_run == -__builtin_inff()) ? 0.0f : m_run; }
+  MHA_MEMBER float msub() const { return m_sub; }
 
   // Distance bias and mask of the scores of the wave's j-th block.
   MHA_MEMBER void bias_and_mask(f32x16 (&s)[NS], int j) const {
@@ -342,6 +344,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 #pragma unroll
     for (int e = 0; e < 16; ++e) w.o[t][e] = 0.0f;
   w.m_run = -__builtin_inff();
+  w.m_sub = 0.0f;
   w.l_run = 0.0f;
   if constexpr (BF16) P::k_offsets(w.ko, li, hi);
 

@@ -111,6 +111,11 @@ struct Geo {
   // swizzles repeat every 16 rows, so each BC-row block of a stage is laid
   // out as a stand-alone tile would be.
   //
+  // The stage's first row goes into the buffer resource (base advanced,
+  // record count shortened, so rows past `bytes` still read as 0): base,
+  // bytes and kb are uniform, so this is scalar work, and each lane's
+  // offset is the same for every stage, computed once.
+  //
   // The loads are issued from inline assembly (M0 set in the same statement)
   // so that the compiler's wait-count pass does not treat every later LDS
   // read as a possible reader of this tile and wait for the loads there;
@@ -119,14 +124,23 @@ struct Geo {
   template <bool IS_K>
   __device__ static inline void stage(uint32_t tile, const T* base, uint32_t bytes, int kb,
                                       int wave, int lane) {
-    const auto rs = make_rsrc(base, bytes);
+    // (readfirstlane states the uniformity, so that the resource is built
+    // in scalar registers, as the instruction requires.)
+    const uint32_t start = (uint32_t)kb * (uint32_t)TILE;
+    const uint64_t addr = (uint64_t)(uintptr_t)base + start;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    // bytes and start stay below 2^31 (a head is under 2 GiB): a signed
+    // difference clamped at 0, which the scalar unit has instructions for.
+    const int rest = (int)bytes - (int)start;
+    const uint32_t left = __builtin_amdgcn_readfirstlane((uint32_t)(rest > 0 ? rest : 0));
+    const auto rs = make_rsrc((const void*)(uintptr_t)(((uint64_t)hi << 32) | lo), left);
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int slot = (u * NW + wave) * 64;  // first chunk of this load
       const int q = slot + lane;
       const int r = q / CPR, pc = q % CPR;
-      const uint32_t off =
-          ((uint32_t)(kb * KS * BC + r) * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
+      const uint32_t off = ((uint32_t)r * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
     }
