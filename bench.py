@@ -612,6 +612,17 @@ def main():
         calibrate_copy(torch, args.calibrate_copy)
         return
 
+    if args.workload not in inputs.WORKLOADS:
+        # One extended or multi-head-layer workload alone (for profiling):
+        # its record, timed like the extended list of the full run.
+        if args.workload in inputs.EXT_WORKLOADS:
+            rec = bench_ext(torch, mha, args.workload, args.steps, args.warmup)
+        elif args.workload in inputs.LAYER_WORKLOADS:
+            rec = bench_layer(torch, mha, args.workload, args.steps, args.warmup)
+        else:
+            ap.error("unknown workload %r" % args.workload)
+        print(json.dumps(rec), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     print("bench: %s steps=%d warmup=%d" % (w.name, args.steps, args.warmup),
           file=sys.stderr, flush=True)
