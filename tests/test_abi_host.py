@@ -346,6 +346,11 @@ def test_forward_kernel_name_follows_the_variant_rule(lib):
     # the long causal workload: 64 query blocks of 256 rows x 16 heads
     assert name(1, 16, 16, 16384, 16384, 128, mode=1) == \
         "mha::attn_fwd_kernel<__bf16, 128, 8, 1, true, false>"
+    # long causal walks at d = 128 keep eight waves; shorter ones take four
+    assert name(2, 16, 16, 8192, 8192, 128, mode=1).endswith("<__bf16, 128, 8, 1, true, false>")
+    assert name(4, 16, 16, 4096, 4096, 128, mode=1).endswith("<__bf16, 128, 4, 1, true, false>")
+    assert name(4, 16, 16, 4096, 4096, 128, mode=0).endswith("<__bf16, 128, 8, 1, false, false>")
+    assert name(8, 8, 8, 2048, 2048, 128, mode=0).endswith("<__bf16, 128, 4, 1, false, false>")
     # n = 128, d = 64: four-wave workgroups; one per 128 rows
     assert name(32, 8, 8, 128, 128, 64) == "mha::attn_fwd_kernel<__bf16, 64, 4, 1, false, false>"
     # few query blocks and a long key axis: two key groups

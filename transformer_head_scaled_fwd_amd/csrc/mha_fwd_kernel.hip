@@ -553,7 +553,7 @@ static hipError_t launch_variant(const LaunchArgs& a) {
 // Workgroup shape as forward_variant (mha_host.cpp) chooses it.
 template <typename T, int D>
 static hipError_t launch_d(const LaunchArgs& a) {
-  const FwdVariant v = forward_variant(sizeof(T) == 2, D, a.B, a.H, a.n, a.m);
+  const FwdVariant v = forward_variant(sizeof(T) == 2, D, a.B, a.H, a.n, a.m, a.mode);
   if constexpr (sizeof(T) == 2) {
     if (v.nw == 8 && v.ks == 1) {
       if constexpr (D == 128) return launch_variant<T, D, 8, 1>(a);

@@ -64,10 +64,12 @@ mha_status check_multihead(const void* Xq, const void* Xk, const void* Xv, const
                     int64_t m, int64_t d_model, int64_t H, mha_dtype dtype);
 
 // Workgroup shape of the forward kernel for a problem: NW waves per
-// workgroup, KS key groups (see the kernel).
+// workgroup, KS key groups (see the kernel).  mode: 0 no causal mask, 1
+// causal top-left, 2 causal bottom-right.
 struct FwdVariant {
   int nw, ks;
 };
-FwdVariant forward_variant(bool bf16, int d, int64_t B, int64_t H, int64_t n, int64_t m);
+FwdVariant forward_variant(bool bf16, int d, int64_t B, int64_t H, int64_t n, int64_t m,
+                           int mode);
 
 }  // namespace mha
