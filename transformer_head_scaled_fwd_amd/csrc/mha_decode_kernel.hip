@@ -151,18 +151,43 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     }
     if constexpr (ALIBI) P::bias(sc, (float)(prow - kb * BC - 4 * hi), sr);
     if (kb * BC + BC > lim_min) P::mask(sc, row_lim - kb * BC - 4 * hi);
-    // Online softmax, not thresholded here: one block per step is cheap.
-    const float mx = pair_max(P::lane_max(sc)) * sl2;
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int ct = 0; ct < D / 32; ++ct)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
+    // Online softmax with the max formed on demand, as in the forward
+    // kernel: the weights are taken against the running max as it stands;
+    // only when a lane's block sum passes 2^16 (or a row meets its first
+    // valid key) does the wave form the block max, raise the running max
+    // (when the block max exceeds it by more than TAU), recompute the
+    // weights and rescale.  With a distance bias the row max rises block
+    // after block, so the max is formed every block.  Most blocks thus
+    // leave the output accumulators alone, for the MFMAs only.
     typename P::PFrag pf;
-    P::weights(pf, sc, sl2, (m_run == -__builtin_inff()) ? 0.0f : m_run, l_run);
+    float lb = 0.0f;
+    auto exact = [&]() {
+      const float mx = pair_max(P::lane_max(sc)) * sl2;
+      const bool grew = mx > m_run + TAU;
+      const float m_new = grew ? mx : m_run;
+      const float alpha =
+          (m_new == -__builtin_inff()) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      lb = 0.0f;
+      P::weights(pf, sc, sl2, (m_run == -__builtin_inff()) ? 0.0f : m_run, lb);
+      P::pin(pf);
+      if (__any(grew)) {
+#pragma unroll
+        for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[ct][e] *= alpha;
+      }
+    };
+    if constexpr (ALIBI) {
+      exact();
+    } else {
+      P::weights(pf, sc, sl2, (m_run == -__builtin_inff()) ? 0.0f : m_run, lb);
+      P::pin(pf);
+      const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && lb > 0.0f);
+      if (__any(slow)) exact();
+    }
+    l_run += lb;
     // V(kb) was issued before K(kb+NW).
     if (more) G1::template wait_loads<LOADS>();
     else G1::template wait_loads<0>();
