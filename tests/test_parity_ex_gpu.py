@@ -76,6 +76,12 @@ CASES = [
     (2, 4, 2, 129, 129, 64, "f32", "top_left", True, (1, 129)),
     (2, 4, 1, 9, 400, 128, "f32", "bottom_right", True, (1, 400)),
     (1, 2, 2, 100, 250, 64, "f32", False, True, None),
+    # causal d = 64 with ALiBi (key walk from the diagonal down): ragged
+    # lengths; bottom-right with rows that see no key; two key groups
+    (2, 8, 4, 520, 520, 64, "bf16", "top_left", True, (1, 520)),
+    (2, 4, 2, 300, 200, 64, "bf16", "bottom_right", True, (10, 200)),
+    (1, 4, 4, 1100, 1100, 64, "bf16", "top_left", True, None),
+    (1, 4, 2, 1200, 1500, 64, "bf16", "bottom_right", True, (700, 1500)),
 ]
 
 
@@ -92,6 +98,82 @@ def test_forward_ex_parity(gpu, B, H, Hkv, n, m, d, dt, causal, alibi, lens):
                                          alibi_slopes=sl, scale=mha.default_scale(d),
                                          return_lse=True)
     assert torch.isfinite(o.float()).all()
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
+    assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
+
+
+def _variant(B, H, Hkv, n, m, d, dt, causal, alibi):
+    code = mha.MHA_BF16 if dt == "bf16" else mha.MHA_F32
+    mode = {False: 0, "top_left": 1, "bottom_right": 2}[causal]
+    return mha.load().mha_forward_kernel_name(B, H, Hkv, n, m, d, code, mode,
+                                              int(alibi)).decode()
+
+
+def _falling_inputs(B, H, n, m, d, dt, step, seed):
+    # Key j lies step * (m - 1 - j) along every query's direction: walked
+    # from the diagonal down to key 0, each 64-key block scores higher than
+    # the one before by 64 * step * scale (46 in log2 units for step 4 at
+    # d = 64, 23 for step 2), more than the slopes below take away, so every
+    # block's weights pass the on-demand bound: block max, raise, rescale.
+    _, _, v, _ = inputs.draw(B, H, n, m, d, d, dt, seed=seed)
+    q = torch.zeros(B, H, n, d)
+    k = torch.zeros(B, H, m, d)
+    q[..., 0] = 1.0
+    k[..., 0] = step * torch.arange(m - 1, -1, -1, dtype=torch.float32)
+    k[..., 1] = torch.linspace(-1, 1, m)
+    q[..., 1] = torch.linspace(1, -1, n)
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    return q.to(dtype), k.to(dtype), v
+
+
+# fp32 takes a smaller step over fewer keys: its scores' exponents reach
+# step * m * scale * log2(e) (72 for step 2, m = 200), whose rounding in fp32
+# (2^-18 relative) must stay inside the 1e-5 tolerance.
+@pytest.mark.parametrize("B,H,n,m,dt,causal,step,variant", [
+    (2, 4, 700, 700, "bf16", "top_left", 4.0, "<__bf16, 64, 4, 1, true, true>"),
+    (1, 4, 1100, 1100, "bf16", "top_left", 4.0, "<__bf16, 64, 8, 2, true, true>"),
+    (2, 4, 300, 900, "bf16", "bottom_right", 4.0, "<__bf16, 64, 4, 1, true, true>"),
+    (1, 2, 200, 200, "f32", "top_left", 2.0, "<float, 64, 4, 1, true, true>"),
+])
+def test_alibi_causal_falling_scores(gpu, B, H, n, m, dt, causal, step, variant):
+    _say("ALiBi falling scores B=%d H=%d n=%d m=%d %s %s step %g"
+         % (B, H, n, m, dt, causal, step))
+    assert _variant(B, H, H, n, m, 64, dt, causal, True).endswith(variant)
+    q, k, v = _falling_inputs(B, H, n, m, 64, dt, step, seed=71)
+    sl = slopes(H)
+    o, lse = gpu_ex(q, k, v, None, causal, sl)
+    o_ref, lse_ref = oracle.attention_ex(q, k, v, causal=causal, alibi_slopes=sl,
+                                         scale=mha.default_scale(64), return_lse=True)
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
+
+
+# Top-left rows past a short sequence's length see only keys far behind
+# them: with slope 8 their lse reaches -4000, where fp32 rounding alone is
+# 2.4e-4, inside the bf16 tolerance but not the fp32 one; fp32 runs without
+# lengths.
+@pytest.mark.parametrize("dt,causal,lens", [
+    ("bf16", "top_left", None),
+    ("bf16", "top_left", (1, 640)),
+    ("bf16", "bottom_right", (200, 640)),
+    ("f32", "top_left", None),
+])
+def test_alibi_causal_steep_slopes(gpu, dt, causal, lens):
+    # Slopes from 8 (a row's weight falls by e^-8 per key of distance, so
+    # far keys underflow to 0) to 0 (no bias), on the d = 64 causal path.
+    B, H, n, m, d = 2, 4, 640, 640, 64
+    _say("ALiBi steep slopes %s %s lens=%s" % (dt, causal, lens))
+    q, k, v, kl = draw(B, H, H, n, m, d, dt, seed=73, lens=lens)
+    # With slope 8 a row's output is nearly its own value row, up to ~4.5
+    # for N(0,1) values, where half a bf16 ulp (2^-6) alone would exceed the
+    # tolerance: halve the values (exact in either type).
+    v = (v.float() * 0.5).to(v.dtype)
+    sl = np.array([8.0, 1.0, 0.03, 0.0], np.float32)
+    o, lse = gpu_ex(q, k, v, kl, causal, sl)
+    o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal=causal,
+                                         alibi_slopes=sl, scale=mha.default_scale(d),
+                                         return_lse=True)
     assert maxerr(o, o_ref, "O") <= TOL_O[dt]
     assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
     assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]

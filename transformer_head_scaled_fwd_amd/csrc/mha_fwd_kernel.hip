@@ -74,6 +74,18 @@ struct Walk {
   using G = Geo<T, D, NW, KS>;
   using P = Phase<T, D>;
   static constexpr int NS = P::NS;
+  // Causal attention with a distance bias walks its keys backwards, from
+  // the diagonal down to key 0.  The bias is then largest in the first
+  // blocks a row sees, so its running max is set there and later blocks
+  // can keep it (the weights-first softmax below); walked forwards, the max
+  // rises block after block towards the diagonal.  d = 64 only: at d = 128
+  // the weights-first step with the bias does not fit the registers.
+  static constexpr bool REV = CAUSAL && ALIBI && D == 64;
+  // With REV, bf16 takes the part of the bias that varies within a block,
+  // sr * (key offset), as the initial value of the score MFMAs (the
+  // accumulator input), so that only a per-row shift is left for the
+  // vector ALU.
+  static constexpr bool BIAS_MFMA = REV && G::BF16;
 
   const char* ktiles;  // LDS: K ring, NSTAGE stages
   const char* vtiles;  // LDS: V ring, NSTAGE stages
@@ -84,6 +96,9 @@ struct Walk {
   int row_lim;         // first invalid key of this lane's row
   int L;               // valid keys of the sequence
   int wave_nkb;        // key blocks this wave reads (its own, every KS-th)
+  int nst;             // ring stages the workgroup walks
+  int j0;              // first step of this wave's walk (0 unless REV)
+  int j1;              // one past its last step
   float sl2;           // scale * log2(e)
   float sr;            // ALiBi slope / scale (raw-score units)
   u32x4 qf[P::NQF];    // Q fragments
@@ -92,6 +107,12 @@ struct Walk {
   float m_run;         // running max of scale*log2(e)*s (per row)
   float m_sub;         // what the weights subtract: m_run, or 0 while it is -inf
   float l_run;         // this lane's share of the row sum
+  f32x16 cb[BIAS_MFMA ? NS : 1];  // BIAS_MFMA: sr * (key offset within the block)
+
+  // Ring stage (of KS blocks) that step j walks.
+  MHA_MEMBER int stage_of(int j) const { return REV ? nst - 1 - j : j; }
+  // Key block of this wave at step j.
+  MHA_MEMBER int block_of(int j) const { return stage_of(j) * KS + kg; }
 
   // gb: key block index (keys gb * BC onwards)
   MHA_MEMBER bool needs_mask(int gb) const {
@@ -132,21 +153,50 @@ struct Walk {
   }
   MHA_MEMBER float msub() const { return m_sub; }
 
-  // Distance bias and mask of the scores of the wave's j-th block.
+  // What the wave's scores at step j exceed their biased values by, in raw
+  // score units: with BIAS_MFMA the scores carry sr * (key offset within
+  // the block) but not the rest of the bias, -sr * (p_i - first key - 4hi),
+  // which is the same for all of a lane's keys of the block (every key a
+  // causal row sees lies at or before it, so the distance is p_i - j).
+  MHA_MEMBER float shift(int j) const {
+    if constexpr (BIAS_MFMA) return sr * (float)(prow - block_of(j) * BC - 4 * hi);
+    else return 0.0f;
+  }
+  // Raw block max of the lane's biased scores at step j.
+  MHA_MEMBER float block_max(const f32x16 (&s)[NS], int j) const {
+    if constexpr (BIAS_MFMA) return P::lane_max(s) - shift(j);
+    else return P::lane_max(s);
+  }
+  // What the weights of step j subtract: the running max, plus the shift.
+  MHA_MEMBER float msub_at(int j) const {
+    if constexpr (BIAS_MFMA) return __builtin_fmaf(sl2, shift(j), m_sub);
+    else return m_sub;
+  }
+
+  // Scores of the tile at kt (with BIAS_MFMA, started from cb).
+  MHA_MEMBER void scores_at(f32x16 (&s)[NS], const char* kt) const {
+    if constexpr (BIAS_MFMA) P::template scores_ko<true>(s, kt, qf, ko, cb);
+    else if constexpr (G::BF16) P::scores_ko(s, kt, qf, ko);
+    else P::scores(s, kt, qf, li, hi);
+  }
+
+  // Distance bias and mask of the scores of the wave's step j.
   MHA_MEMBER void bias_and_mask(f32x16 (&s)[NS], int j) const {
-    const int gb = j * KS + kg;
-    if constexpr (ALIBI) P::bias(s, (float)(prow - gb * BC - 4 * hi), sr);
+    const int gb = block_of(j);
+    if constexpr (ALIBI && !BIAS_MFMA) P::bias(s, (float)(prow - gb * BC - 4 * hi), sr);
     if (needs_mask(gb)) P::mask(s, row_lim - gb * BC - 4 * hi);
   }
 
-  // Scores, mask, running max and weights of the first block (prologue).
-  MHA_MEMBER void first_block(typename P::PFrag& pf) {
+  // Scores, mask, running max and weights of the wave's first block, at
+  // step j (the prologue's, or with REV, the first step of a shorter walk).
+  MHA_MEMBER void first_block(typename P::PFrag& pf, int j) {
     f32x16 s[NS];
-    P::scores(s, k_tile(0), qf, li, hi);
-    bias_and_mask(s, 0);
+    if constexpr (BIAS_MFMA) scores_at(s, k_tile(j));
+    else P::scores(s, k_tile(j), qf, li, hi);
+    bias_and_mask(s, j);
     bool grew;
-    raise_max(pair_max(P::lane_max(s)), grew);  // nothing accumulated yet
-    P::weights(pf, s, sl2, msub(), l_run);
+    raise_max(pair_max(block_max(s, j)), grew);  // nothing accumulated yet
+    P::weights(pf, s, sl2, msub_at(j), l_run);
   }
 
   // PV of the wave's block kb (weights in pf_cur) and, when the wave reads
@@ -160,14 +210,13 @@ struct Walk {
     const int kgo = KS == 1 ? 0 : kg * (BC * G::ROWB);
     const char* kt_next = ktiles + ((ST + 1) % G::NSTAGE) * G::TILE + kgo;
     const char* vt_cur = vtiles + ST * G::TILE + kgo;
-    if (kb + 1 < wave_nkb) {
+    if (kb + 1 < j1) {
       f32x16 s[NS];
-      if constexpr (G::BF16) P::scores_ko(s, kt_next, qf, ko);
-      else P::scores(s, kt_next, qf, li, hi);
+      scores_at(s, kt_next);
       P::prefetch_k();
       bias_and_mask(s, kb + 1);
       P::pv(o, vt_cur, pf_cur, lane);
-      if constexpr (ALIBI) {
+      if constexpr (ALIBI && !REV) {
         // A distance bias raises the row max block after block on the way
         // to the diagonal: form the block max every block.
         bool grew;
@@ -183,14 +232,14 @@ struct Walk {
       // is in this block) the whole wave takes the exact path: raise the
       // max, recompute the weights, rescale.
       float lb = 0.0f;
-      P::weights(pf_nxt, s, sl2, msub(), lb);
+      P::weights(pf_nxt, s, sl2, msub_at(kb + 1), lb);
       P::pin(pf_nxt);
       const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && lb > 0.0f);
       if (__any(slow)) {
         bool grew;
-        const float alpha = raise_max(pair_max(P::lane_max(s)), grew);
+        const float alpha = raise_max(pair_max(block_max(s, kb + 1)), grew);
         lb = 0.0f;
-        P::weights(pf_nxt, s, sl2, msub(), lb);
+        P::weights(pf_nxt, s, sl2, msub_at(kb + 1), lb);
         P::pin(pf_nxt);
         rescale_output(alpha, grew);
       }
@@ -310,6 +359,11 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // them that belong to the wave's key group.
   const int vis = CAUSAL ? max(0, min(nkb, (w.prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
   w.wave_nkb = vis > w.kg ? (vis - w.kg + KS - 1) / KS : 0;
+  // Steps of the wave: the first wave_nkb forwards; backwards (REV), the
+  // last wave_nkb, a shorter walk starting later (past the end if empty).
+  w.nst = nst;
+  w.j0 = W::REV ? (w.wave_nkb > 0 ? nst - w.wave_nkb : nst + 1) : 0;
+  w.j1 = W::REV ? nst : w.wave_nkb;
   w.row_lim = CAUSAL ? min(L, my_row + off + 1) : L;
   w.sl2 = prm.scale_log2;
   w.sr = ALIBI ? alibi_slopes[t] / prm.scale : 0.0f;
@@ -325,10 +379,12 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
 
   // Loads of ring stage j of the keys and of the values into their slots.
   auto load_k = [&](int j) {
-    G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, j, wave, lane);
+    G::template stage<true>(lds_k + (j % G::NSTAGE) * G::TILE, kbase, kv_bytes, w.stage_of(j),
+                            wave, lane);
   };
   auto load_v = [&](int j) {
-    G::template stage<false>(lds_v + (j % G::NSTAGE) * G::TILE, vbase, kv_bytes, j, wave, lane);
+    G::template stage<false>(lds_v + (j % G::NSTAGE) * G::TILE, vbase, kv_bytes, w.stage_of(j),
+                             wave, lane);
   };
 
   // The first key/value blocks, then the wait for Q; the wait before the
@@ -347,6 +403,12 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   w.m_sub = 0.0f;
   w.l_run = 0.0f;
   if constexpr (BF16) P::k_offsets(w.ko, li, hi);
+  if constexpr (W::BIAS_MFMA) {
+#pragma unroll
+    for (int jt = 0; jt < W::NS; ++jt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.cb[jt][e] = w.sr * (float)(32 * jt + 8 * (e / 4) + e % 4);
+  }
 
   // Pipeline: iteration kb reads K(kb+1) and V(kb).  It issues the loads of
   // K(kb+1+DIST) and V(kb+DIST), which go to the ring slots of K(kb) and
@@ -358,7 +420,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   if (nst > 0) {
     G::template wait_loads<0>();
     __syncthreads();
-    if (0 < w.wave_nkb) w.first_block(pa);
+    if (W::REV ? (w.j0 == 0) : (0 < w.wave_nkb)) w.first_block(pa, 0);
     // K(0) is consumed before its slot is refilled, by the load of stage
     // 1 + NSTAGE - 1 in the first iteration; a walk of at most NSTAGE
     // stages never refills it.
@@ -393,11 +455,21 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   for (int kb = 0; kb < nst; kb += 2) {
     int issued = issue(kb);
     static_assert(G::NSTAGE == 2, "the loop alternates two ring stages");
-    if (kb < w.wave_nkb) w.template step<0>(kb, pa, pb);
+    if constexpr (W::REV) {
+      if (kb + 1 == w.j0) w.first_block(pb, kb + 1);
+      else if (kb >= w.j0) w.template step<0>(kb, pa, pb);
+    } else if (kb < w.wave_nkb) {
+      w.template step<0>(kb, pa, pb);
+    }
     publish(issued);
     if (kb + 1 >= nst) break;
     issued = issue(kb + 1);
-    if (kb + 1 < w.wave_nkb) w.template step<1>(kb + 1, pb, pa);
+    if constexpr (W::REV) {
+      if (kb + 2 == w.j0) w.first_block(pa, kb + 2);
+      else if (kb + 1 >= w.j0) w.template step<1>(kb + 1, pb, pa);
+    } else if (kb + 1 < w.wave_nkb) {
+      w.template step<1>(kb + 1, pb, pa);
+    }
     publish(issued);
   }
 

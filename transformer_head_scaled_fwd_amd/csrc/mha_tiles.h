@@ -231,13 +231,20 @@ struct Phase {
       asm volatile("" : "+v"(ko[ks]));
     }
   }
+  // With INIT the accumulators start from c0 instead of 0 (the MFMA adds
+  // its accumulator input, so a per-element term costs no vector ALU).
+  template <bool INIT = false>
   MHA_INLINE void scores_ko(f32x16 (&s)[NS], const char* kt, const u32x4 (&qf)[NQF],
-                            const uint32_t (&ko)[NKO]) {
+                            const uint32_t (&ko)[NKO], const f32x16* c0 = nullptr) {
     static_assert(BF16, "precomputed K offsets: bf16 tiles");
 #pragma unroll
     for (int jt = 0; jt < NS; ++jt) {
+      if constexpr (INIT) {
+        s[jt] = c0[jt];
+      } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
+        for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
+      }
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(kt + jt * 32 * ROWB + ko[ks]);
