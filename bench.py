@@ -64,13 +64,22 @@ def valid_pairs(w, key_lens) -> int:
     return total * w.H
 
 
+def kernel_code(text: str) -> str:
+    """The code of a C++ source without its comments and with every run of
+    white space made one blank: what the compiler sees of it."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the forward kernel's sources (the kernel file and the shared
-    device header it includes)."""
+    """Hash of the forward kernel's code (the kernel file and the shared
+    device header it includes), comments and layout excluded, so that a
+    profile stays matched to a kernel whose comments alone changed."""
     h = hashlib.sha256()
     for p in KERNEL_SRCS:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(kernel_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 

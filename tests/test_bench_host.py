@@ -91,3 +91,12 @@ def test_cpu_baseline_runs_the_whole_workload_or_distinct_rows():
     np.testing.assert_array_equal(ref, full[rows[:, 0], rows[:, 1], rows[:, 2]])
     rec = bench.parity(w, host, host[0].new_zeros(host[0].shape), rows=rows, ref=ref)
     assert rec["compared"] == "%d sampled rows" % len(rows)
+
+
+def test_kernel_hash_ignores_comments_only():
+    # The profiles' kernel hash is taken over the code with comments and
+    # layout removed: a comment or a blank line leaves it, a token changes it.
+    code = "int f(int x) {  // twice\n  return 2 * x; /* doubled */\n}\n"
+    assert bench.kernel_code(code) == "int f(int x) { return 2 * x; }"
+    assert bench.kernel_code(code.replace("// twice", "// two times")) == bench.kernel_code(code)
+    assert bench.kernel_code(code.replace("2 * x", "3 * x")) != bench.kernel_code(code)

@@ -26,8 +26,10 @@
 //            weights are taken against the running max as it stands; only
 //            when one of them could exceed 2^16 (its lane's block sum does)
 //            is the block max formed, the running max raised and the output
-//            rescaled.  With a distance bias, whose row max rises block after
-//            block towards the diagonal, the block max is formed every block;
+//            rescaled.  A distance bias raises a row's max block after block
+//            towards the diagonal: causal rows at d = 64 therefore walk their
+//            keys backwards, from the diagonal down, and keep the weights-
+//            first path; elsewhere the block max is formed every block;
 //   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype; the V
 //            operand comes straight from the row-major tile through the
 //            LDS transpose read (ds_read_b64_tr_b16).
