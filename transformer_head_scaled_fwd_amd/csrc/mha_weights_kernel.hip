@@ -40,8 +40,15 @@ struct WeightParams {
   float scale_log2;      // scale * log2(e)
 };
 
+// Resident workgroups per CU: two, except fp32 with d = 128, whose K ring and
+// staging take 98 KiB of LDS.
+template <typename T, int D>
+constexpr int weights_wg_per_cu() {
+  return (sizeof(T) == 4 && D == 128) ? 1 : 2;
+}
+
 template <typename T, int D, bool CAUSAL, bool ALIBI>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, (weights_wg_per_cu<T, D>()))
 attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
                     const int32_t* __restrict__ key_lens, const float* __restrict__ alibi_slopes,
                     const float* __restrict__ lse, T* __restrict__ Ap, WeightParams prm) {
