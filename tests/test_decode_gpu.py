@@ -42,6 +42,10 @@ CASES = [
     (64, 16, 16, 1, 256, 64, "bf16", False, (100, 256)),     # no split: direct store
     (2, 8, 2, 2, 1000, 128, "f32", True, (500, 1000)),
     (2, 4, 4, 1, 700, 64, "f32", False, None),
+    # one sequence, MQA, a long cache: 128 splits per row, merged by four
+    # waves per row; and a ragged pair with 40 splits and ALiBi
+    (1, 32, 1, 1, 32768, 128, "bf16", False, None),
+    (2, 8, 1, 1, 20000, 64, "bf16", True, (9000, 20000)),
 ]
 
 

@@ -256,18 +256,28 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   }
 }
 
-// Merge of the splits: one wave per query row.  Lane s holds split s's
-// running max and row sum (64 splits at a time), so the row's max M and the
-// weighted sum come from one round of loads and two wave reductions; the
-// unnormalised outputs are then summed with the lanes over the features,
-// eight splits' loads in flight at a time.
-template <typename T, int D>
+// Merge of the splits: CW waves per query row (a 256-thread workgroup holds
+// 4 / CW rows).  Every wave forms the row's max M over all splits (lane s
+// holds split s's running max, 64 splits at a time, then a wave reduction);
+// wave w of a row then sums the splits of its own share, [w * per,
+// (w + 1) * per), weighted by 2^(m_s - M): lanes over the features, eight
+// splits' loads in flight at a time.  With CW > 1 the waves' sums meet in LDS
+// and the row's first wave adds them in wave order, so the result does not
+// depend on timing.  Many splits (a long cache over few rows) take CW = 4:
+// the shares shorten the chain of dependent loads a row needs.
+template <typename T, int D, int CW>
 __global__ void __launch_bounds__(256)
 attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
                            T* __restrict__ Op, float* __restrict__ lse, int rows, int nsplit) {
-  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + threadIdx.x / 64);
+  constexpr int FL = D / 64;  // features per lane
+  constexpr int RPW = 4 / CW;  // rows per workgroup
+  __shared__ float acc_w[CW > 1 ? CW : 1][CW > 1 ? D : 1];
+  __shared__ float lsum_w[CW];
+  const int w4 = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
+  const int row = blockIdx.x * RPW + w4 / CW;
+  const int wave = w4 % CW;
   const int lane = threadIdx.x % 64;
-  if (row >= rows) return;
+  if (CW == 1 && row >= rows) return;
   const float* ml = part_ml + (size_t)row * nsplit * 2;
   const float* po = part_o + (size_t)row * nsplit * D;
   float M = -__builtin_inff();
@@ -275,48 +285,70 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
     if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+  const int per = (nsplit + CW - 1) / CW;
+  const int sb = wave * per, se = min(nsplit, sb + per);
   float lsum = 0.0f;
-  float acc[D / 64];
+  float acc[FL];
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u) acc[u] = 0.0f;
-  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+  for (int u = 0; u < FL; ++u) acc[u] = 0.0f;
+  for (int s0 = sb; s0 < se; s0 += 64) {
     // This lane's split: its weight 2^(m_s - M) (0 for a split with no key).
     float f = 0.0f;
-    if (s0 + lane < nsplit) {
+    if (s0 + lane < se) {
       const float ms = ml[2 * (s0 + lane)];
       f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
       lsum += f * ml[2 * (s0 + lane) + 1];
     }
-    const int cnt = min(64, nsplit - s0);
+    const int cnt = min(64, se - s0);
     int j = 0;
     for (; j + 8 <= cnt; j += 8) {
-      float v[8][D / 64];
+      float v[8][FL];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
 #pragma unroll
-        for (int u = 0; u < D / 64; ++u) v[q][u] = po[(size_t)(s0 + j + q) * D + lane + 64 * u];
+        for (int u = 0; u < FL; ++u) v[q][u] = po[(size_t)(s0 + j + q) * D + lane + 64 * u];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float fq = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j + q));
 #pragma unroll
-        for (int u = 0; u < D / 64; ++u) acc[u] += fq * v[q][u];
+        for (int u = 0; u < FL; ++u) acc[u] += fq * v[q][u];
       }
     }
     for (; j < cnt; ++j) {
       const float fq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
 #pragma unroll
-      for (int u = 0; u < D / 64; ++u) acc[u] += fq * po[(size_t)(s0 + j) * D + lane + 64 * u];
+      for (int u = 0; u < FL; ++u) acc[u] += fq * po[(size_t)(s0 + j) * D + lane + 64 * u];
     }
   }
 #pragma unroll
   for (int x = 32; x >= 1; x >>= 1) lsum += __shfl_xor(lsum, x);
-  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+  float total = lsum;
+  float sum[FL];
 #pragma unroll
-  for (int u = 0; u < D / 64; ++u) Op[(size_t)row * D + lane + 64 * u] = (T)(acc[u] * inv);
+  for (int u = 0; u < FL; ++u) sum[u] = acc[u];
+  if constexpr (CW > 1) {
+#pragma unroll
+    for (int u = 0; u < FL; ++u) acc_w[wave][lane + 64 * u] = acc[u];
+    if (lane == 0) lsum_w[wave] = lsum;
+    __syncthreads();
+    if (wave != 0) return;
+    total = 0.0f;
+#pragma unroll
+    for (int u = 0; u < FL; ++u) sum[u] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      total += lsum_w[w];
+#pragma unroll
+      for (int u = 0; u < FL; ++u) sum[u] += acc_w[w][lane + 64 * u];
+    }
+  }
+  const float inv = (total > 0.0f) ? 1.0f / total : 0.0f;
+#pragma unroll
+  for (int u = 0; u < FL; ++u) Op[(size_t)row * D + lane + 64 * u] = (T)(sum[u] * inv);
   if (lane == 0 && lse != nullptr)
-    lse[row] = (lsum > 0.0f) ? 0.6931471805599453f * (M + __builtin_amdgcn_logf(lsum))
-                             : -__builtin_inff();
+    lse[row] = (total > 0.0f) ? 0.6931471805599453f * (M + __builtin_amdgcn_logf(total))
+                              : -__builtin_inff();
 }
 
 // Waves per workgroup: four, except fp32 with d = 128, whose tiles allow two.
@@ -352,9 +384,14 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int64_t rows = a.B * a.H * a.n;
-  hipLaunchKernelGGL((attn_decode_combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)),
-                     dim3(256), 0, (hipStream_t)a.stream, part_o, part_ml, (T*)a.O, a.lse,
-                     (int)rows, (int)p.nsplit);
+  if (p.nsplit > 16)
+    hipLaunchKernelGGL((attn_decode_combine_kernel<T, D, 4>), dim3((unsigned)rows), dim3(256), 0,
+                       (hipStream_t)a.stream, part_o, part_ml, (T*)a.O, a.lse, (int)rows,
+                       (int)p.nsplit);
+  else
+    hipLaunchKernelGGL((attn_decode_combine_kernel<T, D, 1>), dim3((unsigned)((rows + 3) / 4)),
+                       dim3(256), 0, (hipStream_t)a.stream, part_o, part_ml, (T*)a.O, a.lse,
+                       (int)rows, (int)p.nsplit);
   return hipGetLastError();
 }
 

@@ -74,11 +74,13 @@ mha_status check_decode_sizes(int64_t B, int64_t H, int64_t H_kv, int64_t n, int
   if (!head_fits(n, d * es) || !head_fits(m, d * es) || !head_fits(mul_sat(H, n), d * es))
     return MHA_ERR_UNSUPPORTED;
   const int64_t rows = mul_sat(mul_sat(B, H), n);
-  if (rows > INT32_MAX || !grid_fits((rows + 3) / 4, 256)) return MHA_ERR_UNSUPPORTED;
+  if (rows > INT32_MAX) return MHA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || n == 0) return MHA_OK;
   const mha::DecodePlan p = mha::plan_decode(B, H, H_kv, n, m, (int)d, bf16);
   if (!grid_fits(mul_sat(mul_sat(mul_sat(B, H_kv), p.nrs), p.nsplit), 256))
     return MHA_ERR_UNSUPPORTED;
+  // the split merge: one 256-thread workgroup per query row
+  if (p.nsplit > 1 && !grid_fits(rows, 256)) return MHA_ERR_UNSUPPORTED;
   return MHA_OK;
 }
 
