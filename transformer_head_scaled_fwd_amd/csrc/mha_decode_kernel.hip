@@ -200,20 +200,25 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   G1::template wait_loads<0>();
 
   // ---- merge the waves' partial results through LDS ----
+  // Only the row set's real rows (R - 32 rs of them, at most 32) are merged:
+  // a single decoded token over one K/V head (R = 1) leaves 31 lanes idle.
   const float l_tot = pair_sum(l_run);
+  const int rows_here = min(kRowsPerWave, prm.R - rs * kRowsPerWave);
   __syncthreads();  // every wave is done with its tiles
   float* mo = reinterpret_cast<float*>(smem);  // [NW][32][D]
   float* mm = mo + NW * kRowsPerWave * D;      // [NW][32]
   float* ml = mm + NW * kRowsPerWave;          // [NW][32]
+  if (li < rows_here) {
 #pragma unroll
-  for (int ct = 0; ct < D / 32; ++ct)
+    for (int ct = 0; ct < D / 32; ++ct)
 #pragma unroll
-    for (int gg = 0; gg < 4; ++gg) {
-      f32x4 v;
+      for (int gg = 0; gg < 4; ++gg) {
+        f32x4 v;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = o[ct][4 * gg + q];
-      *reinterpret_cast<f32x4*>(mo + (wave * kRowsPerWave + li) * D + ct * 32 + 8 * gg + 4 * hi) = v;
-    }
+        for (int q = 0; q < 4; ++q) v[q] = o[ct][4 * gg + q];
+        *reinterpret_cast<f32x4*>(mo + (wave * kRowsPerWave + li) * D + ct * 32 + 8 * gg + 4 * hi) = v;
+      }
+  }
   if (hi == 0) {
     mm[wave * kRowsPerWave + li] = m_run;
     ml[wave * kRowsPerWave + li] = l_tot;
@@ -222,10 +227,9 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
 
   const bool direct = prm.nsplit == 1;
   const size_t q_batch = (size_t)b * prm.H * n;  // first query row of batch b
-  for (int e = tid; e < kRowsPerWave * D; e += 64 * NW) {
+  for (int e = tid; e < rows_here * D; e += 64 * NW) {
     const int row = e / D, c = e % D;
     const int rr = rs * kRowsPerWave + row;
-    if (rr >= prm.R) continue;
     float M = -__builtin_inff();
 #pragma unroll
     for (int w = 0; w < NW; ++w) M = fmaxf(M, mm[w * kRowsPerWave + row]);
