@@ -76,12 +76,16 @@ CASES = [
     (2, 4, 2, 129, 129, 64, "f32", "top_left", True, (1, 129)),
     (2, 4, 1, 9, 400, 128, "f32", "bottom_right", True, (1, 400)),
     (1, 2, 2, 100, 250, 64, "f32", False, True, None),
-    # causal d = 64 with ALiBi (key walk from the diagonal down): ragged
-    # lengths; bottom-right with rows that see no key; two key groups
+    # causal with ALiBi (key walk from the diagonal down): ragged lengths;
+    # bottom-right with rows that see no key; two key groups; d = 128
     (2, 8, 4, 520, 520, 64, "bf16", "top_left", True, (1, 520)),
     (2, 4, 2, 300, 200, 64, "bf16", "bottom_right", True, (10, 200)),
     (1, 4, 4, 1100, 1100, 64, "bf16", "top_left", True, None),
     (1, 4, 2, 1200, 1500, 64, "bf16", "bottom_right", True, (700, 1500)),
+    (2, 8, 2, 600, 600, 128, "bf16", "top_left", True, (1, 600)),
+    (2, 4, 2, 300, 900, 128, "bf16", "bottom_right", True, (200, 900)),
+    (1, 4, 4, 1200, 1200, 128, "bf16", "top_left", True, None),
+    (1, 4, 2, 300, 300, 128, "f32", "top_left", True, (1, 300)),
 ]
 
 
@@ -114,8 +118,10 @@ def _falling_inputs(B, H, n, m, d, dt, step, seed):
     # Key j lies step * (m - 1 - j) along every query's direction: walked
     # from the diagonal down to key 0, each 64-key block scores higher than
     # the one before by 64 * step * scale (46 in log2 units for step 4 at
-    # d = 64, 23 for step 2), more than the slopes below take away, so every
-    # block's weights pass the on-demand bound: block max, raise, rescale.
+    # d = 64, 23 for step 2; 33 for step 4 at d = 128, 24 for step 3), more
+    # than the slopes below take away (at d = 128 they are divided by 8), so
+    # every block's weights pass the on-demand bound: block max, raise,
+    # rescale.
     _, _, v, _ = inputs.draw(B, H, n, m, d, d, dt, seed=seed)
     q = torch.zeros(B, H, n, d)
     k = torch.zeros(B, H, m, d)
@@ -128,23 +134,40 @@ def _falling_inputs(B, H, n, m, d, dt, step, seed):
 
 
 # fp32 takes a smaller step over fewer keys: its scores' exponents reach
-# step * m * scale * log2(e) (72 for step 2, m = 200), whose rounding in fp32
-# (2^-18 relative) must stay inside the 1e-5 tolerance.
-@pytest.mark.parametrize("B,H,n,m,dt,causal,step,variant", [
-    (2, 4, 700, 700, "bf16", "top_left", 4.0, "<__bf16, 64, 4, 1, true, true>"),
-    (1, 4, 1100, 1100, "bf16", "top_left", 4.0, "<__bf16, 64, 8, 2, true, true>"),
-    (2, 4, 300, 900, "bf16", "bottom_right", 4.0, "<__bf16, 64, 4, 1, true, true>"),
-    (1, 2, 200, 200, "f32", "top_left", 2.0, "<float, 64, 4, 1, true, true>"),
+# step * m * scale * log2(e) (72 for step 2, m = 200; 76 for step 3 at
+# d = 128), whose rounding in fp32 (2^-18 relative) must stay inside the
+# 1e-5 tolerance.
+@pytest.mark.parametrize("B,H,n,m,d,dt,causal,step,variant", [
+    (2, 4, 700, 700, 64, "bf16", "top_left", 4.0, "<__bf16, 64, 4, 1, true, true>"),
+    (1, 4, 1100, 1100, 64, "bf16", "top_left", 4.0, "<__bf16, 64, 8, 2, true, true>"),
+    (2, 4, 300, 900, 64, "bf16", "bottom_right", 4.0, "<__bf16, 64, 4, 1, true, true>"),
+    (1, 2, 200, 200, 64, "f32", "top_left", 2.0, "<float, 64, 4, 1, true, true>"),
+    # d = 128: eight waves over 256 rows (the oracle on sampled rows), four
+    # waves, two key groups, fp32
+    (2, 16, 8192, 8192, 128, "bf16", "top_left", 4.0, "<__bf16, 128, 8, 1, true, true>"),
+    (4, 16, 1024, 1024, 128, "bf16", "top_left", 4.0, "<__bf16, 128, 4, 1, true, true>"),
+    (1, 4, 320, 1280, 128, "bf16", "bottom_right", 4.0, "<__bf16, 128, 8, 2, true, true>"),
+    (1, 2, 200, 200, 128, "f32", "top_left", 3.0, "<float, 128, 4, 1, true, true>"),
 ])
-def test_alibi_causal_falling_scores(gpu, B, H, n, m, dt, causal, step, variant):
-    _say("ALiBi falling scores B=%d H=%d n=%d m=%d %s %s step %g"
-         % (B, H, n, m, dt, causal, step))
-    assert _variant(B, H, H, n, m, 64, dt, causal, True).endswith(variant)
-    q, k, v = _falling_inputs(B, H, n, m, 64, dt, step, seed=71)
-    sl = slopes(H)
+def test_alibi_causal_falling_scores(gpu, B, H, n, m, d, dt, causal, step, variant):
+    _say("ALiBi falling scores B=%d H=%d n=%d m=%d d=%d %s %s step %g"
+         % (B, H, n, m, d, dt, causal, step))
+    assert _variant(B, H, H, n, m, d, dt, causal, True).endswith(variant)
+    q, k, v = _falling_inputs(B, H, n, m, d, dt, step, seed=71)
+    sl = slopes(H) if d == 64 else slopes(H) / 8
     o, lse = gpu_ex(q, k, v, None, causal, sl)
-    o_ref, lse_ref = oracle.attention_ex(q, k, v, causal=causal, alibi_slopes=sl,
-                                         scale=mha.default_scale(64), return_lse=True)
+    if B * H * n * m <= 1 << 27:
+        o_ref, lse_ref = oracle.attention_ex(q, k, v, causal=causal, alibi_slopes=sl,
+                                             scale=mha.default_scale(d), return_lse=True)
+    else:
+        rng = np.random.Generator(np.random.PCG64(72))
+        flat = rng.choice(B * H * n, size=768, replace=False)
+        rows = np.stack([flat // (H * n), (flat // n) % H, flat % n], 1)
+        rows = np.concatenate([rows, [[B - 1, H - 1, n - 1], [0, 0, 0]]]).astype(np.int64)
+        o_ref, lse_ref = oracle.attention_ex_rows(q, k, v, rows, causal=causal, alibi_slopes=sl,
+                                                  scale=mha.default_scale(d))
+        sel = tuple(torch.from_numpy(rows[:, c]) for c in range(3))
+        o, lse = o[sel], lse[sel]
     assert maxerr(o, o_ref, "O") <= TOL_O[dt]
     assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
 
@@ -153,17 +176,20 @@ def test_alibi_causal_falling_scores(gpu, B, H, n, m, dt, causal, step, variant)
 # them: with slope 8 their lse reaches -4000, where fp32 rounding alone is
 # 2.4e-4, inside the bf16 tolerance but not the fp32 one; fp32 runs without
 # lengths.
-@pytest.mark.parametrize("dt,causal,lens", [
-    ("bf16", "top_left", None),
-    ("bf16", "top_left", (1, 640)),
-    ("bf16", "bottom_right", (200, 640)),
-    ("f32", "top_left", None),
+@pytest.mark.parametrize("d,dt,causal,lens", [
+    (64, "bf16", "top_left", None),
+    (64, "bf16", "top_left", (1, 640)),
+    (64, "bf16", "bottom_right", (200, 640)),
+    (64, "f32", "top_left", None),
+    (128, "bf16", "top_left", (1, 640)),
+    (128, "bf16", "bottom_right", (200, 640)),
+    (128, "f32", "top_left", None),
 ])
-def test_alibi_causal_steep_slopes(gpu, dt, causal, lens):
+def test_alibi_causal_steep_slopes(gpu, d, dt, causal, lens):
     # Slopes from 8 (a row's weight falls by e^-8 per key of distance, so
-    # far keys underflow to 0) to 0 (no bias), on the d = 64 causal path.
-    B, H, n, m, d = 2, 4, 640, 640, 64
-    _say("ALiBi steep slopes %s %s lens=%s" % (dt, causal, lens))
+    # far keys underflow to 0) to 0 (no bias), on the causal path.
+    B, H, n, m = 2, 4, 640, 640
+    _say("ALiBi steep slopes d=%d %s %s lens=%s" % (d, dt, causal, lens))
     q, k, v, kl = draw(B, H, H, n, m, d, dt, seed=73, lens=lens)
     # With slope 8 a row's output is nearly its own value row, up to ~4.5
     # for N(0,1) values, where half a bf16 ulp (2^-6) alone would exceed the

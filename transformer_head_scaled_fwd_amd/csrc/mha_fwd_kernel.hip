@@ -27,9 +27,9 @@
 //            when one of them could exceed 2^16 (its lane's block sum does)
 //            is the block max formed, the running max raised and the output
 //            rescaled.  A distance bias raises a row's max block after block
-//            towards the diagonal: causal rows at d = 64 therefore walk their
-//            keys backwards, from the diagonal down, and keep the weights-
-//            first path; elsewhere the block max is formed every block;
+//            towards the diagonal: causal rows therefore walk their keys
+//            backwards, from the diagonal down, and keep the weights-first
+//            path; without a mask the block max is formed every block;
 //   PV       O^T += V^T P^T on MFMA with P rounded to the input dtype; the V
 //            operand comes straight from the row-major tile through the
 //            LDS transpose read (ds_read_b64_tr_b16).
@@ -80,13 +80,12 @@ struct Walk {
   // the diagonal down to key 0.  The bias is then largest in the first
   // blocks a row sees, so its running max is set there and later blocks
   // can keep it (the weights-first softmax below); walked forwards, the max
-  // rises block after block towards the diagonal.  d = 64 only: at d = 128
-  // the weights-first step with the bias does not fit the registers.
-  static constexpr bool REV = CAUSAL && ALIBI && D == 64;
-  // With REV, bf16 takes the part of the bias that varies within a block,
-  // sr * (key offset), as the initial value of the score MFMAs (the
-  // accumulator input), so that only a per-row shift is left for the
-  // vector ALU.
+  // rises block after block towards the diagonal.
+  static constexpr bool REV = CAUSAL && ALIBI;
+  // With REV, bf16 takes the part of the bias that varies within a 32-key
+  // tile, sr * (key offset within the tile), as the initial value of the
+  // score MFMAs (the accumulator input, the same for every tile), so that
+  // only a per-row shift per tile is left for the vector ALU.
   static constexpr bool BIAS_MFMA = REV && G::BF16;
 
   const char* ktiles;  // LDS: K ring, NSTAGE stages
@@ -99,7 +98,7 @@ struct Walk {
   int L;               // valid keys of the sequence
   int wave_nkb;        // key blocks this wave reads (its own, every KS-th)
   int nst;             // ring stages the workgroup walks
-  int j0;              // first step of this wave's walk (0 unless REV)
+  int j0;              // first step of this wave's walk: 0, or past the end if empty
   int j1;              // one past its last step
   float sl2;           // scale * log2(e)
   float sr;            // ALiBi slope / scale (raw-score units)
@@ -109,7 +108,7 @@ struct Walk {
   float m_run;         // running max of scale*log2(e)*s (per row)
   float m_sub;         // what the weights subtract: m_run, or 0 while it is -inf
   float l_run;         // this lane's share of the row sum
-  f32x16 cb[BIAS_MFMA ? NS : 1];  // BIAS_MFMA: sr * (key offset within the block)
+  f32x16 cb;           // BIAS_MFMA: sr * (key offset within the 32-key tile)
 
   // Ring stage (of KS blocks) that step j walks.
   MHA_MEMBER int stage_of(int j) const { return REV ? nst - 1 - j : j; }
@@ -155,29 +154,43 @@ struct Walk {
   }
   MHA_MEMBER float msub() const { return m_sub; }
 
-  // What the wave's scores at step j exceed their biased values by, in raw
-  // score units: with BIAS_MFMA the scores carry sr * (key offset within
-  // the block) but not the rest of the bias, -sr * (p_i - first key - 4hi),
-  // which is the same for all of a lane's keys of the block (every key a
-  // causal row sees lies at or before it, so the distance is p_i - j).
-  MHA_MEMBER float shift(int j) const {
-    if constexpr (BIAS_MFMA) return sr * (float)(prow - block_of(j) * BC - 4 * hi);
+  // What the wave's scores of tile jt at step j exceed their biased values
+  // by, in raw score units: with BIAS_MFMA the scores carry sr * (key
+  // offset within the tile) but not the rest of the bias,
+  // -sr * (p_i - first key of the tile - 4hi), which is the same for all of
+  // a lane's keys of the tile (every key a causal row sees lies at or before
+  // it, so the distance is p_i - j).
+  MHA_MEMBER float shift(int j, int jt) const {
+    if constexpr (BIAS_MFMA) return sr * (float)(prow - block_of(j) * BC - 32 * jt - 4 * hi);
     else return 0.0f;
   }
   // Raw block max of the lane's biased scores at step j.
   MHA_MEMBER float block_max(const f32x16 (&s)[NS], int j) const {
-    if constexpr (BIAS_MFMA) return P::lane_max(s) - shift(j);
-    else return P::lane_max(s);
+    if constexpr (BIAS_MFMA) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int jt = 0; jt < NS; ++jt) mx = fmaxf(mx, P::tile_max(s[jt]) - shift(j, jt));
+      return mx;
+    } else {
+      return P::lane_max(s);
+    }
   }
-  // What the weights of step j subtract: the running max, plus the shift.
-  MHA_MEMBER float msub_at(int j) const {
-    if constexpr (BIAS_MFMA) return __builtin_fmaf(sl2, shift(j), m_sub);
-    else return m_sub;
+  // Weights of the scores of step j against the running max m_sub (with
+  // BIAS_MFMA, plus each tile's shift).
+  MHA_MEMBER void weights_at(typename P::PFrag& pf, const f32x16 (&s)[NS], int j, float& l) const {
+    if constexpr (BIAS_MFMA) {
+      float ms[NS];
+#pragma unroll
+      for (int jt = 0; jt < NS; ++jt) ms[jt] = __builtin_fmaf(sl2, shift(j, jt), m_sub);
+      P::weights(pf, s, sl2, ms, l);
+    } else {
+      P::weights(pf, s, sl2, m_sub, l);
+    }
   }
 
   // Scores of the tile at kt (with BIAS_MFMA, started from cb).
   MHA_MEMBER void scores_at(f32x16 (&s)[NS], const char* kt) const {
-    if constexpr (BIAS_MFMA) P::template scores_ko<true>(s, kt, qf, ko, cb);
+    if constexpr (BIAS_MFMA) P::template scores_ko<true>(s, kt, qf, ko, &cb);
     else if constexpr (G::BF16) P::scores_ko(s, kt, qf, ko);
     else P::scores(s, kt, qf, li, hi);
   }
@@ -190,7 +203,7 @@ struct Walk {
   }
 
   // Scores, mask, running max and weights of the wave's first block, at
-  // step j (the prologue's, or with REV, the first step of a shorter walk).
+  // step j.
   MHA_MEMBER void first_block(typename P::PFrag& pf, int j) {
     f32x16 s[NS];
     if constexpr (BIAS_MFMA) scores_at(s, k_tile(j));
@@ -198,7 +211,7 @@ struct Walk {
     bias_and_mask(s, j);
     bool grew;
     raise_max(pair_max(block_max(s, j)), grew);  // nothing accumulated yet
-    P::weights(pf, s, sl2, msub_at(j), l_run);
+    weights_at(pf, s, j, l_run);
   }
 
   // PV of the wave's block kb (weights in pf_cur) and, when the wave reads
@@ -234,14 +247,14 @@ struct Walk {
       // is in this block) the whole wave takes the exact path: raise the
       // max, recompute the weights, rescale.
       float lb = 0.0f;
-      P::weights(pf_nxt, s, sl2, msub_at(kb + 1), lb);
+      weights_at(pf_nxt, s, kb + 1, lb);
       P::pin(pf_nxt);
       const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && lb > 0.0f);
       if (__any(slow)) {
         bool grew;
         const float alpha = raise_max(pair_max(block_max(s, kb + 1)), grew);
         lb = 0.0f;
-        P::weights(pf_nxt, s, sl2, msub_at(kb + 1), lb);
+        weights_at(pf_nxt, s, kb + 1, lb);
         P::pin(pf_nxt);
         rescale_output(alpha, grew);
       }
@@ -361,10 +374,15 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   // them that belong to the wave's key group.
   const int vis = CAUSAL ? max(0, min(nkb, (w.prow_w + kRowsPerWave + BC - 1) / BC)) : nkb;
   w.wave_nkb = vis > w.kg ? (vis - w.kg + KS - 1) / KS : 0;
-  // Steps of the wave: the first wave_nkb forwards; backwards (REV), the
-  // last wave_nkb, a shorter walk starting later (past the end if empty).
+  // Steps of the wave: the first wave_nkb forwards.  Backwards (REV) every
+  // wave with a key to see walks all the workgroup's stages from the
+  // diagonal down: the first one or two stages lie past the last key of a
+  // wave whose rows end before them and are masked out whole for it, which
+  // costs their MFMAs but keeps the first block out of the loop (and the
+  // registers of a second first-block path with it).  An empty walk starts
+  // past the end.
   w.nst = nst;
-  w.j0 = W::REV ? (w.wave_nkb > 0 ? nst - w.wave_nkb : nst + 1) : 0;
+  w.j0 = W::REV ? (w.wave_nkb > 0 ? 0 : nst + 1) : 0;
   w.j1 = W::REV ? nst : w.wave_nkb;
   w.row_lim = CAUSAL ? min(L, my_row + off + 1) : L;
   w.sl2 = prm.scale_log2;
@@ -407,9 +425,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   if constexpr (BF16) P::k_offsets(w.ko, li, hi);
   if constexpr (W::BIAS_MFMA) {
 #pragma unroll
-    for (int jt = 0; jt < W::NS; ++jt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) w.cb[jt][e] = w.sr * (float)(32 * jt + 8 * (e / 4) + e % 4);
+    for (int e = 0; e < 16; ++e) w.cb[e] = w.sr * (float)(8 * (e / 4) + e % 4);
   }
 
   // Pipeline: iteration kb reads K(kb+1) and V(kb).  It issues the loads of
@@ -458,8 +474,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     int issued = issue(kb);
     static_assert(G::NSTAGE == 2, "the loop alternates two ring stages");
     if constexpr (W::REV) {
-      if (kb + 1 == w.j0) w.first_block(pb, kb + 1);
-      else if (kb >= w.j0) w.template step<0>(kb, pa, pb);
+      if (kb >= w.j0) w.template step<0>(kb, pa, pb);
     } else if (kb < w.wave_nkb) {
       w.template step<0>(kb, pa, pb);
     }
@@ -467,8 +482,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     if (kb + 1 >= nst) break;
     issued = issue(kb + 1);
     if constexpr (W::REV) {
-      if (kb + 2 == w.j0) w.first_block(pa, kb + 2);
-      else if (kb + 1 >= w.j0) w.template step<1>(kb + 1, pb, pa);
+      if (kb + 1 >= w.j0) w.template step<1>(kb + 1, pb, pa);
     } else if (kb + 1 < w.wave_nkb) {
       w.template step<1>(kb + 1, pb, pa);
     }

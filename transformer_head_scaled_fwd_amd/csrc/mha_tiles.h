@@ -231,8 +231,9 @@ struct Phase {
       asm volatile("" : "+v"(ko[ks]));
     }
   }
-  // With INIT the accumulators start from c0 instead of 0 (the MFMA adds
-  // its accumulator input, so a per-element term costs no vector ALU).
+  // With INIT every tile's accumulators start from *c0 instead of 0 (the
+  // MFMA adds its accumulator input, so a per-element term costs no vector
+  // ALU).
   template <bool INIT = false>
   MHA_INLINE void scores_ko(f32x16 (&s)[NS], const char* kt, const u32x4 (&qf)[NQF],
                             const uint32_t (&ko)[NKO], const f32x16* c0 = nullptr) {
@@ -240,7 +241,7 @@ struct Phase {
 #pragma unroll
     for (int jt = 0; jt < NS; ++jt) {
       if constexpr (INIT) {
-        s[jt] = c0[jt];
+        s[jt] = *c0;
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[jt][e] = 0.0f;
@@ -310,14 +311,23 @@ struct Phase {
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[jt][e]);
     return mx;
   }
+  // The same over the lane's keys of one 32-key tile.
+  MHA_INLINE float tile_max(const f32x16& s) {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    return mx;
+  }
 
-  // p = 2^(s * scale * log2e - msub), rounded to the PV operand type; the
-  // lane's share of the row sum accumulates the rounded values.
+  // p = 2^(s * scale * log2e - msub[jt]) for the keys of score tile jt,
+  // rounded to the PV operand type; the lane's share of the row sum
+  // accumulates the rounded values.
   //
   // bf16: slice k (16 keys, k = 0..3) takes tile jt = k/2, groups
   // g = 2(k%2) and 2(k%2)+1: lane half hi holds keys 16k + 4hi + r (k-slots
   // 8hi + r) and 16k + 8 + 4hi + r (k-slots 8hi + 4 + r), r = 0..3.
-  MHA_INLINE void weights(PFrag& pf, const f32x16 (&s)[NS], float sl2, float msub, float& l) {
+  MHA_INLINE void weights(PFrag& pf, const f32x16 (&s)[NS], float sl2, const float (&msub)[NS],
+                          float& l) {
     if constexpr (BF16) {
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -326,8 +336,8 @@ struct Phase {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int g = g0 + e / 4, r = e % 4;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r], sl2, -msub));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r + 1], sl2, -msub));
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r], sl2, -msub[jt]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][4 * g + r + 1], sl2, -msub[jt]));
           const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
           l = __builtin_amdgcn_fdot2_f32_bf16(pk, ones, l, false);
           pf[k][e] = pk[0];
@@ -339,11 +349,18 @@ struct Phase {
       for (int jt = 0; jt < NS; ++jt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][e], sl2, -msub));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[jt][e], sl2, -msub[jt]));
           pf[jt][e] = p;
           l += p;
         }
     }
+  }
+  // The same subtrahend for every tile.
+  MHA_INLINE void weights(PFrag& pf, const f32x16 (&s)[NS], float sl2, float msub, float& l) {
+    float ms[NS];
+#pragma unroll
+    for (int jt = 0; jt < NS; ++jt) ms[jt] = msub;
+    weights(pf, s, sl2, ms, l);
   }
 
   // O^T += V^T P^T for the value tile at vt.
