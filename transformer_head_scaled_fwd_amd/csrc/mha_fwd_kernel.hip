@@ -607,7 +607,11 @@ static hipError_t launch_one(const LaunchArgs& a) {
   prm.nqb = (int)((a.n + BR - 1) / BR);
   prm.bottom_right = a.mode == 2;
   // XCD pinning of K/V heads (see the kernel) when they split evenly over
-  // the 8 XCDs; unit_group: enough K/V heads per XCD to fill its 32 CUs.
+  // the 8 XCDs.  unit_group: enough K/V heads per XCD to fill its 32 CUs;
+  // causal, further up to the most heads whose K/V rows stay within twice
+  // an XCD's 4 MB L2: the XCD then runs heaviest first across more heads,
+  // which balances query blocks of unequal work over its CUs, while their
+  // K/V rows still mostly hit in L2.
   const int64_t units = a.B * a.H_kv;
   prm.units_per_xcd = 0;
   prm.unit_group = 1;
@@ -620,6 +624,12 @@ static hipError_t launch_one(const LaunchArgs& a) {
     prm.units_per_xcd = (int)(units / 8);
     while ((int64_t)prm.unit_group * per_unit < slots && prm.units_per_xcd % (2 * prm.unit_group) == 0)
       prm.unit_group *= 2;
+    if (a.mode != 0) {
+      const int64_t unit_bytes = a.m * a.d * 2 * (int64_t)sizeof(T);  // K and V rows of a head
+      while (prm.units_per_xcd % (2 * prm.unit_group) == 0 &&
+             2 * prm.unit_group * unit_bytes <= ((int64_t)8 << 20))
+        prm.unit_group *= 2;
+    }
   }
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
