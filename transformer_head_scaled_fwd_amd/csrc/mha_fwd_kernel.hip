@@ -276,6 +276,7 @@ struct FwdParams {
   int unit_group;     // K/V heads one XCD works on at a time
   float scale;        // the caller's scale
   float scale_log2;   // scale * log2(e)
+  int stream_out;     // results written through to memory (kStoreOut)
 };
 
 // Resident workgroups per CU: one for 8 waves, or when the fp32 d = 128
@@ -531,8 +532,8 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     const float v = (l_tot > 0.0f) ? 0.6931471805599453f * (w.m_run + __builtin_amdgcn_logf(l_tot))
                                    : -__builtin_inff();
     const auto rl = make_rsrc(lse + (size_t)bh * n, (uint32_t)n * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rl,
-                                          (int)((uint32_t)my_row * 4), 0, 0);
+    store_result(__builtin_bit_cast(uint32_t, v), rl, (int)((uint32_t)my_row * 4),
+                 prm.stream_out);
   }
   // O rows staged in LDS when they fit the (now idle) K/V ring, past the
   // merge area, rows padded by 16 bytes, then stored 16 bytes per lane:
@@ -573,7 +574,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * OSR + c * 16);
       // rows >= n fall outside the O resource and are dropped
       const uint32_t off = ((uint32_t)(row_w + rr) * D) * ES + c * 16;
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+      store_result(v, ro, (int)off, prm.stream_out);
     }
   } else {
 #pragma unroll
@@ -585,12 +586,12 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
           bf16x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = (__bf16)(w.o[ct][4 * g + r] * inv);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, (int)off, 0, 0);
+          store_result(__builtin_bit_cast(u32x2, v), ro, (int)off, prm.stream_out);
         } else {
           f32x4 v;
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = w.o[ct][4 * g + r] * inv;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, (int)off, 0, 0);
+          store_result(__builtin_bit_cast(u32x4, v), ro, (int)off, prm.stream_out);
         }
       }
   }
@@ -634,6 +635,8 @@ static hipError_t launch_one(const LaunchArgs& a) {
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
+  // Results streamed to memory when they fit the L2s (kStoreOut).
+  prm.stream_out = a.B * a.H * a.n * a.d * (int64_t)sizeof(T) <= kStreamOutMaxBytes;
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, KS, CAUSAL, ALIBI>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K,
                      (const T*)a.V, a.key_lens, a.alibi_slopes, (T*)a.O, a.lse, prm);

@@ -38,6 +38,7 @@ struct WeightParams {
   int vec8;              // 1 when m % 8 == 0: rows staged through LDS, 16-byte stores
   float scale;           // the caller's scale
   float scale_log2;      // scale * log2(e)
+  int stream_out;        // A written through to memory (kStoreOut)
 };
 
 // Resident workgroups per CU: two, except fp32 with d = 128, whose K ring and
@@ -134,14 +135,12 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
             bf16x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (__bf16)p[4 * g + r];
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ra,
-                                                  (int)(off_el * ES), 0, 0);
+            store_result(__builtin_bit_cast(u32x2, v), ra, (int)(off_el * ES), prm.stream_out);
           } else {
             f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = p[4 * g + r];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ra,
-                                                   (int)(off_el * ES), 0, 0);
+            store_result(__builtin_bit_cast(u32x4, v), ra, (int)(off_el * ES), prm.stream_out);
           }
         }
       } else {
@@ -150,14 +149,14 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
           if (key + r < m) {
             if constexpr (BF16) {
               const __bf16 h = (__bf16)p[4 * g + r];
-              __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), ra,
-                                                    (int)((off_el + r) * ES), 0, 0);
+              store_result(__builtin_bit_cast(uint16_t, h), ra, (int)((off_el + r) * ES),
+                           prm.stream_out);
             } else {
               // (the element is copied out first: a bit cast taken straight
               // from a vector element reads element 0 of the group here)
               const float x = p[4 * g + r];
-              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), ra,
-                                                    (int)((off_el + r) * ES), 0, 0);
+              store_result(__builtin_bit_cast(uint32_t, x), ra, (int)((off_el + r) * ES),
+                           prm.stream_out);
             }
           }
         }
@@ -178,7 +177,7 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
       const int key = kb * BC + c * (16 / ES);
       if (key < m) {
         const uint32_t off_el = (uint32_t)(row_w + rr) * (uint32_t)m + (uint32_t)key;
-        __builtin_amdgcn_raw_buffer_store_b128(chunk_of(rr, c), ra, (int)(off_el * ES), 0, 0);
+        store_result(chunk_of(rr, c), ra, (int)(off_el * ES), prm.stream_out);
       }
     }
   };
@@ -288,6 +287,8 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.vec8 = (a.m % 8) == 0;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
+  // A streamed to memory when it fits the L2s (kStoreOut).
+  prm.stream_out = a.B * a.H * a.n * a.m * (int64_t)sizeof(T) <= kStreamOutMaxBytes;
   const int64_t blocks = units * nkc;
   hipLaunchKernelGGL((attn_weights_kernel<T, D, CAUSAL, ALIBI>), dim3((unsigned)blocks), dim3(256),
                      0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, a.key_lens,
