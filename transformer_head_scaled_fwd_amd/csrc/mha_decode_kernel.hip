@@ -268,7 +268,10 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
 // splits' loads in flight at a time.  With CW > 1 the waves' sums meet in LDS
 // and the row's first wave adds them in wave order, so the result does not
 // depend on timing.  Many splits (a long cache over few rows) take CW = 4:
-// the shares shorten the chain of dependent loads a row needs.
+// the shares shorten the chain of dependent loads a row needs.  Up to
+// kOneWaveSplits splits take one wave per row that issues all of the row's
+// loads at once.
+constexpr int kOneWaveSplits = 16;  // most splits a row merges with one wave (CW = 1)
 template <typename T, int D, int CW>
 __global__ void __launch_bounds__(256)
 attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -285,44 +288,72 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
   const float* ml = part_ml + (size_t)row * nsplit * 2;
   const float* po = part_o + (size_t)row * nsplit * D;
   float M = -__builtin_inff();
-  for (int s0 = 0; s0 < nsplit; s0 += 64)
-    if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
-#pragma unroll
-  for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
-  const int per = (nsplit + CW - 1) / CW;
-  const int sb = wave * per, se = min(nsplit, sb + per);
   float lsum = 0.0f;
   float acc[FL];
 #pragma unroll
   for (int u = 0; u < FL; ++u) acc[u] = 0.0f;
-  for (int s0 = sb; s0 < se; s0 += 64) {
-    // This lane's split: its weight 2^(m_s - M) (0 for a split with no key).
-    float f = 0.0f;
-    if (s0 + lane < se) {
-      const float ms = ml[2 * (s0 + lane)];
-      f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      lsum += f * ml[2 * (s0 + lane) + 1];
+  if constexpr (CW == 1) {
+    // At most kOneWaveSplits splits: every load of the row is issued at
+    // once (split q >= nsplit reads split nsplit - 1 again, weighted 0), so
+    // the row waits for one round trip to memory instead of three.
+    float mv = -__builtin_inff(), lv = 0.0f;
+    if (lane < nsplit) {
+      mv = ml[2 * lane];
+      lv = ml[2 * lane + 1];
     }
-    const int cnt = min(64, se - s0);
-    int j = 0;
-    for (; j + 8 <= cnt; j += 8) {
-      float v[8][FL];
+    float v[kOneWaveSplits][FL];
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < kOneWaveSplits; ++q)
 #pragma unroll
-        for (int u = 0; u < FL; ++u) v[q][u] = po[(size_t)(s0 + j + q) * D + lane + 64 * u];
+      for (int u = 0; u < FL; ++u) v[q][u] = po[(size_t)min(q, nsplit - 1) * D + lane + 64 * u];
+    M = mv;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float fq = __builtin_bit_cast(
-            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j + q));
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    const float f = (mv == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(mv - M);
+    lsum = f * lv;
 #pragma unroll
-        for (int u = 0; u < FL; ++u) acc[u] += fq * v[q][u];
+    for (int q = 0; q < kOneWaveSplits; ++q) {
+      const float fq =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), q));
+#pragma unroll
+      for (int u = 0; u < FL; ++u) acc[u] += fq * v[q][u];
+    }
+  } else {
+    for (int s0 = 0; s0 < nsplit; s0 += 64)
+      if (s0 + lane < nsplit) M = fmaxf(M, ml[2 * (s0 + lane)]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    const int per = (nsplit + CW - 1) / CW;
+    const int sb = wave * per, se = min(nsplit, sb + per);
+    for (int s0 = sb; s0 < se; s0 += 64) {
+      // This lane's split: its weight 2^(m_s - M) (0 for a split with no key).
+      float f = 0.0f;
+      if (s0 + lane < se) {
+        const float ms = ml[2 * (s0 + lane)];
+        f = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        lsum += f * ml[2 * (s0 + lane) + 1];
       }
-    }
-    for (; j < cnt; ++j) {
-      const float fq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+      const int cnt = min(64, se - s0);
+      int j = 0;
+      for (; j + 8 <= cnt; j += 8) {
+        float v[8][FL];
 #pragma unroll
-      for (int u = 0; u < FL; ++u) acc[u] += fq * po[(size_t)(s0 + j) * D + lane + 64 * u];
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int u = 0; u < FL; ++u) v[q][u] = po[(size_t)(s0 + j + q) * D + lane + 64 * u];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float fq = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j + q));
+#pragma unroll
+          for (int u = 0; u < FL; ++u) acc[u] += fq * v[q][u];
+        }
+      }
+      for (; j < cnt; ++j) {
+        const float fq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j));
+#pragma unroll
+        for (int u = 0; u < FL; ++u) acc[u] += fq * po[(size_t)(s0 + j) * D + lane + 64 * u];
+      }
     }
   }
 #pragma unroll
@@ -388,7 +419,7 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   const int64_t rows = a.B * a.H * a.n;
-  if (p.nsplit > 16)
+  if (p.nsplit > kOneWaveSplits)
     hipLaunchKernelGGL((attn_decode_combine_kernel<T, D, 4>), dim3((unsigned)rows), dim3(256), 0,
                        (hipStream_t)a.stream, part_o, part_ml, (T*)a.O, a.lse, (int)rows,
                        (int)p.nsplit);
