@@ -34,16 +34,19 @@ constexpr float TAU = 8.0f;
 // Buffer resource word 3 for gfx9-family raw buffers (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
 // Cache policy of the kernels' result stores (the aux operand of the buffer
-// store builtins): sc0 | nt | sc1, written through to memory as streaming
-// data instead of being held dirty in the XCD's L2 until the kernel ends.
-// Results are read by the next kernel or the host, not by this one.  It
-// pays when a launch's results fit the L2s (8 x 4 MB): held there, they are
-// written back at the end of the kernel, after its last workgroup, which
-// lengthens short launches by several microseconds.  Results well beyond
-// the L2s leave it during the kernel anyway, and writing them through costs
-// more than it saves (measured on the weights pass: 17-34 MB of output
-// 7-11% faster streamed, 67-134 MB 3-5% slower).
-constexpr int kStoreOut = 1 | 2 | 16;
+// store builtins): sc0 | sc1, written through to memory instead of being
+// held dirty in the XCD's L2 until the kernel ends.  Results are read by the
+// next kernel or the host, not by this one.  It pays when a launch's
+// results fit the L2s (8 x 4 MB): held there, they are written back at the
+// end of the kernel, after its last workgroup, which lengthens short
+// launches by several microseconds.  Results well beyond the L2s leave it
+// during the kernel anyway, and writing them through costs more than it
+// saves (measured on the weights pass: 17-34 MB of output 7-11% faster,
+// 67-134 MB 3-5% slower).  The non-temporal bit (nt) as well would make the
+// short launches a little faster still, but the kernel that reads the
+// results next then finds them further away (the multi-head layer's output
+// projection after the core: the layer 3% slower instead of 3% faster).
+constexpr int kStoreOut = 1 | 16;
 constexpr int64_t kStreamOutMaxBytes = (int64_t)48 << 20;
 
 #define MHA_INLINE __device__ static inline __attribute__((always_inline))
