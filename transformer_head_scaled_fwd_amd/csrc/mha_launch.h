@@ -83,6 +83,7 @@ struct ProjProblem {
 };
 struct ProjBatch {
   ProjProblem p[3];
+  int stream_out;    // C written through to memory (set by launch_proj)
 };
 hipError_t launch_proj(const ProjBatch& b, int count, bool bf16, bool a_heads, bool c_heads,
                        void* stream);

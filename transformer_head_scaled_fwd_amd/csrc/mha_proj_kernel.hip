@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
         const int rr = rep * 8 + lane / 8, c = lane % 8;
         const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * SR + c * 16);
         const uint32_t off = c_off((uint32_t)(row0 + 64 * wr + rr), (uint32_t)(col0 + 64 * wc + 8 * c));
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, (int)(off * ES), 0, 0);
+        store_result(v, rc, (int)(off * ES), batch.stream_out);
       }
     }
   } else {
@@ -276,14 +276,18 @@ __global__ void __launch_bounds__(256, 2) proj_gemm_kernel(ProjBatch batch) {
           f32x4 o4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) o4[r] = acc[jn][im][4 * g + r] + bv[jn][g][r];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), rc, (int)(off * ES), 0, 0);
+          store_result(__builtin_bit_cast(u32x4, o4), rc, (int)(off * ES), batch.stream_out);
         }
     }
   }
 }
 
 template <typename T, bool A_HEADS, bool C_HEADS>
-static hipError_t launch_proj_t(const ProjBatch& b, int count, void* stream) {
+static hipError_t launch_proj_t(const ProjBatch& b_in, int count, void* stream) {
+  ProjBatch b = b_in;
+  int64_t out_bytes = 0;
+  for (int i = 0; i < count; ++i) out_bytes += (int64_t)b.p[i].M * b.p[i].N * (int64_t)sizeof(T);
+  b.stream_out = out_bytes <= kStreamOutMaxBytes;
   int tiles = 0;
   for (int i = 0; i < count; ++i) {
     const int t = ((b.p[i].M + proj::BM - 1) / proj::BM) * ((b.p[i].N + proj::BN - 1) / proj::BN);
