@@ -131,8 +131,8 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
 
   int kb = kb0 + wave;
   if (kb < kb_end) {
-    G1::template stage<true>(kt_lds, kbase, kv_bytes, kb, 0, lane);
-    G1::template stage<false>(vt_lds, vbase, kv_bytes, kb, 0, lane);
+    G1::template stage<true, true>(kt_lds, kbase, kv_bytes, kb, 0, lane);
+    G1::template stage<false, true>(vt_lds, vbase, kv_bytes, kb, 0, lane);
   }
   u32x4 qf[P::NQF];
   P::load_q(qf, rq, qrow, hi);
@@ -147,7 +147,7 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     // this wave's LDS reads before the direct loads overwrite the tile.
     if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      G1::template stage<true>(kt_lds, kbase, kv_bytes, kb + NW, 0, lane);
+      G1::template stage<true, true>(kt_lds, kbase, kv_bytes, kb + NW, 0, lane);
     }
     if constexpr (ALIBI) P::bias(sc, (float)(prow - kb * BC - 4 * hi), sr);
     if (kb * BC + BC > lim_min) P::mask(sc, row_lim - kb * BC - 4 * hi);
@@ -194,7 +194,7 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     P::pv(o, vtile, pf, lane);
     if (more) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      G1::template stage<false>(vt_lds, vbase, kv_bytes, kb + NW, 0, lane);
+      G1::template stage<false, true>(vt_lds, vbase, kv_bytes, kb + NW, 0, lane);
     }
   }
   G1::template wait_loads<0>();

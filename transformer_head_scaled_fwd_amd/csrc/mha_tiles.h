@@ -155,7 +155,10 @@ struct Geo {
   // read as a possible reader of this tile and wait for the loads there;
   // the kernel waits for them explicitly before the barrier that publishes
   // the tile.
-  template <bool IS_K>
+  //
+  // STREAM marks the loads non-temporal (nt), for rows that no other
+  // workgroup reads again: a decode step's cache rows.
+  template <bool IS_K, bool STREAM = false>
   __device__ static inline void stage(uint32_t tile, const T* base, uint32_t bytes, int kb,
                                       int wave, int lane) {
     // (readfirstlane states the uniformity, so that the resource is built
@@ -175,8 +178,12 @@ struct Geo {
       const int q = slot + lane;
       const int r = q / CPR, pc = q % CPR;
       const uint32_t off = ((uint32_t)r * D) * ES + (pc ^ (IS_K ? S::k(r) : S::v(r))) * 16;
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
+      if constexpr (STREAM)
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                     :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
+      else
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(tile + slot * 16), "v"(off), "s"(rs) : "memory");
     }
   }
 
