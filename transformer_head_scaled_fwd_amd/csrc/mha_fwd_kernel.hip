@@ -635,7 +635,7 @@ static hipError_t launch_one(const LaunchArgs& a) {
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
-  // Results streamed to memory when they fit the L2s (kStoreOut).
+  // Results written through to memory when they fit the L2s (kStoreOut).
   prm.stream_out = a.B * a.H * a.n * a.d * (int64_t)sizeof(T) <= kStreamOutMaxBytes;
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, NW, KS, CAUSAL, ALIBI>), dim3((unsigned)blocks),
                      dim3(64 * NW), 0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K,

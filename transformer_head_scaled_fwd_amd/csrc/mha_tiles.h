@@ -41,11 +41,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 // end of the kernel, after its last workgroup, which lengthens short
 // launches by several microseconds.  Results well beyond the L2s leave it
 // during the kernel anyway, and writing them through costs more than it
-// saves (measured on the weights pass: 17-34 MB of output 7-11% faster,
-// 67-134 MB 3-5% slower).  The non-temporal bit (nt) as well would make the
-// short launches a little faster still, but the kernel that reads the
-// results next then finds them further away (the multi-head layer's output
-// projection after the core: the layer 3% slower instead of 3% faster).
+// saves (measured on the weights pass, with the non-temporal bit as well:
+// 17-34 MB of output 7-11% faster, 67-134 MB 3-5% slower).  The
+// non-temporal bit (nt) would make the short launches a little faster
+// still, but the kernel that reads the results next then finds them further
+// away (the multi-head layer's output projection after the core: the layer
+// 3% slower instead of 3% faster).
 constexpr int kStoreOut = 1 | 16;
 constexpr int64_t kStreamOutMaxBytes = (int64_t)48 << 20;
 
@@ -61,8 +62,8 @@ __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
-// A result store at byte offset off of r: streamed (kStoreOut) or with the
-// default policy.
+// A result store at byte offset off of r: written through (kStoreOut) or
+// with the default policy.
 __device__ inline void store_result(u32x4 v, __amdgpu_buffer_rsrc_t r, int off, bool stream) {
   if (stream) __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreOut);
   else __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);

@@ -287,7 +287,7 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.vec8 = (a.m % 8) == 0;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
-  // A streamed to memory when it fits the L2s (kStoreOut).
+  // A written through to memory when it fits the L2s (kStoreOut).
   prm.stream_out = a.B * a.H * a.n * a.m * (int64_t)sizeof(T) <= kStreamOutMaxBytes;
   const int64_t blocks = units * nkc;
   hipLaunchKernelGGL((attn_weights_kernel<T, D, CAUSAL, ALIBI>), dim3((unsigned)blocks), dim3(256),
