@@ -275,10 +275,14 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.m = (int)a.m;
   prm.nqb = (int)((a.n + BR - 1) / BR);
   prm.nkb_all = (int)((a.m + BC - 1) / BC);
-  // Key chunks: enough workgroups for about four per CU (a workgroup walks
-  // its chunk's blocks serially, one wave per SIMD each), but whole blocks.
+  // Key chunks (whole blocks; a workgroup walks its chunk's blocks serially,
+  // one wave per SIMD each): without a mask, enough workgroups to fill the
+  // CUs once (B8 H8 n = m = 512 9.10 -> 8.58 us against four per CU,
+  // B2 H8 n = 256 m = 2048 d = 128 8.92 -> 7.16 us); causal, about four per
+  // CU, whose chunks of unequal work then balance over the CUs.
   const int64_t units = (int64_t)((a.n + BR - 1) / BR) * a.B * a.H;
-  const int64_t want = (4 * 256 + units - 1) / units;
+  const int64_t per_cu = a.mode == 0 ? weights_wg_per_cu<T, D>() : 4;
+  const int64_t want = (per_cu * 256 + units - 1) / units;
   const int64_t nkc0 = want < 1 ? 1 : (want > prm.nkb_all ? prm.nkb_all : want);
   prm.kchunk = prm.nkb_all > 0 ? (int)((prm.nkb_all + nkc0 - 1) / nkc0) : 1;
   const int64_t nkc = prm.nkb_all > 0 ? (prm.nkb_all + prm.kchunk - 1) / prm.kchunk : 1;
