@@ -143,3 +143,119 @@ def test_eight_wave_noncausal_key_padding(gpu):
     _say("  %d rows: O max_abs_err=%.3e" % (len(rows), e))
     assert torch.isfinite(o.float()).all()
     assert e <= TOL_O["bf16"]
+
+
+# --- a sweep over the launch variants -------------------------------------------
+#
+# The small sweep above runs the four-wave workgroups almost everywhere.  These
+# cases draw larger shapes so that each lands on a chosen variant of the
+# forward kernel, as the launcher's rule picks it: (0) four-wave workgroups on
+# walks of 1000-3000 keys, fp32 at times, (1) eight-wave workgroups (at least
+# 1024 of 256 rows and an average walk of 48 blocks or more), (2) two key
+# groups (at most 256 workgroups of 128 rows and m >= 1024).  The 18 cases
+# take every variant with every mask mode, with and without ALiBi; grouped K/V
+# heads and key lengths are drawn as above.  The eight-wave cases
+# also write outputs larger than the L2s hold, the others smaller ones, so both
+# result-store policies run.  Each case compares sampled rows (block edges, the
+# last row, random ones) of O and the log-sum-exp with the oracle.
+
+VARIANT_TAG = {0: ", 4, 1, ", 1: ", 8, 1, ", 2: ", 8, 2, "}
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def _vcase(i):
+    """Shape and options of variant-sweep case i (a pure function of i)."""
+    rng = np.random.Generator(np.random.PCG64(50_000 + i))
+    kind = i % 3
+    mode = MODES[(i // 3) % 3]
+    alibi = i >= 9
+    dt = "bf16"
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    if kind == 0:
+        dt = "f32" if rng.random() < 0.5 else "bf16"
+        d = int(rng.choice([64, 128]))
+        n = int(rng.integers(1000, 3001))
+        m = n if mode == "top_left" else int(rng.integers(max(n, 1000) if mode else 1000, 3001))
+        c = _cdiv(n, 128)
+        H = Hkv * g
+        # 256 < ceil(n/128) * B * H < 1024: neither two key groups nor 8 waves.
+        lo = max(1, _cdiv(257, c * H))
+        B = int(rng.integers(lo, max(lo, 1023 // (c * H)) + 1))
+    elif kind == 1:
+        d = 128
+        if mode is False:
+            n, m, g = int(rng.integers(1025, 1401)), int(rng.integers(3072, 4601)), 8
+        elif mode == "top_left":
+            n = m = int(rng.integers(5888, 7201))
+            g = max(g, 2)
+        else:
+            n, g = int(rng.integers(769, 2001)), 8
+            m = n // 2 + int(rng.integers(2944, 4201))
+        H = Hkv * g
+        B = _cdiv(1024, _cdiv(n, 256) * H)
+    else:
+        d = int(rng.choice([64, 128]))
+        if mode == "top_left":
+            n = m = int(rng.integers(1024, 3001))
+        else:
+            m = int(rng.integers(1024, 5001))
+            n = min(int(rng.integers(1, 701)), m)
+        cap = 256 // _cdiv(n, 128)
+        while Hkv * g > cap:
+            if g > 1:
+                g //= 2
+            else:
+                Hkv //= 2
+        H = Hkv * g
+        B = int(rng.integers(1, min(cap // H, max(1, 24_000_000 // (Hkv * m * d))) + 1))
+    lens = None
+    if rng.random() < 0.5:
+        lens = (int(rng.integers(0, m + 1)) if rng.random() < 0.2 else int(rng.integers(m // 2, m + 1)), m)
+    return dict(kind=kind, B=B, H=H, Hkv=Hkv, n=n, m=m, d=d, dt=dt, mode=mode, alibi=alibi,
+                lens=lens, seed=60_000 + i)
+
+
+def _vrows(c, rng):
+    """Sampled (b, t, i): the first and last head, random heads, and in each the
+    rows at workgroup and wave edges, the last row and random rows."""
+    B, H, n = c["B"], c["H"], c["n"]
+    heads = {(0, 0), (B - 1, H - 1)} | {(int(rng.integers(0, B)), int(rng.integers(0, H)))
+                                        for _ in range(6)}
+    edges = {0, 1, 31, 32, 63, 64, 127, 128, 255, 256, n - 2, n - 1}
+    rows = []
+    for b, t in sorted(heads):
+        ii = {i for i in edges if 0 <= i < n} | set(rng.integers(0, n, 6).tolist())
+        rows += [[b, t, i] for i in sorted(ii)]
+    return np.array(rows, np.int64)
+
+
+@pytest.mark.parametrize("i", range(18))
+def test_variant_sweep(gpu, i):
+    c = _vcase(i)
+    code = mha.MHA_BF16 if c["dt"] == "bf16" else mha.MHA_F32
+    name = mha.load().mha_forward_kernel_name(c["B"], c["H"], c["Hkv"], c["n"], c["m"], c["d"],
+                                              code, mha.mask_mode(c["mode"]),
+                                              int(c["alibi"])).decode()
+    _say("variant sweep case %d: %s -> %s" % (i, c, name))
+    assert VARIANT_TAG[c["kind"]] in name
+    q, k, v, kl, sl = _draw(c)
+    o, lse = mha.forward_ex(q.to(DEV), k.to(DEV), v.to(DEV), key_lens=_dev(kl),
+                            causal=c["mode"], alibi_slopes=_dev(sl), return_lse=True)
+    rows = _vrows(c, np.random.Generator(np.random.PCG64(70_000 + i)))
+    ri = torch.as_tensor(rows, device=DEV)
+    got_o = o[ri[:, 0], ri[:, 1], ri[:, 2]].cpu()
+    got_lse = lse[ri[:, 0], ri[:, 1], ri[:, 2]].cpu()
+    finite = bool(torch.isfinite(o.float()).all())
+    torch.cuda.synchronize()
+    ref_o, ref_lse = oracle.attention_ex_rows(q, k, v, rows, key_lens=kl, causal=c["mode"],
+                                              alibi_slopes=sl)
+    eo, el = _maxerr(got_o, ref_o), _maxerr(got_lse, ref_lse)
+    _say("  %d rows: O max_abs_err=%.3e  lse max_abs_err=%.3e" % (len(rows), eo, el))
+    assert finite
+    assert np.array_equal(np.isneginf(oracle.to_f64(got_lse)), np.isneginf(ref_lse))
+    assert eo <= TOL_O[c["dt"]]
+    assert el <= TOL_LSE[c["dt"]]
