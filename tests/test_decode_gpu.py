@@ -13,7 +13,7 @@ import torch
 import oracle
 import transformer_head_scaled_fwd_amd as mha
 from transformer_head_scaled_fwd_amd import inputs
-from test_parity_ex_gpu import TOL_LSE, TOL_O, draw, maxerr
+from test_parity_ex_gpu import TOL_LSE, TOL_O, draw, far_inputs, maxerr
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -164,3 +164,36 @@ def test_decode_binding_rejects_host_workspace(gpu):
     with pytest.raises(ValueError):
         mha.decode(q.to(DEV), k.to(DEV), v.to(DEV), cache_lens=torch.as_tensor(kl).to(DEV),
                    workspace=host_ws)
+
+
+# Decode without ALiBi takes every block on the weights-first path, the first
+# included: a row with no running max yet must take the exact path at its
+# first block with a valid key, even when its weights against 0 all
+# underflow to 0 (scores far below 0, see far_inputs).  A wave holds 32 query
+# rows of one K/V head; rows past the head's group * n are padding lanes with
+# q = 0, whose first block always takes the exact path for the whole wave,
+# so the cases that matter fill all 32 rows (group * n = 32).  fp32 compares
+# O only, as in the forward test.
+@pytest.mark.parametrize("B,H,Hkv,n,m,d,dt,alibi,lens", [
+    (1, 32, 1, 1, 700, 64, "bf16", False, None),             # MQA, one full row set
+    (2, 8, 1, 4, 5000, 128, "bf16", False, (2000, 5000)),    # full row set, split
+    (1, 16, 1, 3, 900, 64, "bf16", False, (1, 900)),         # a full set and a partial one
+    (1, 32, 1, 1, 300, 64, "f32", False, (1, 300)),
+    (2, 8, 2, 1, 700, 64, "bf16", False, None),              # padding lanes in every wave
+    (2, 8, 2, 2, 900, 128, "bf16", True, (400, 900)),        # ALiBi: exact every block
+])
+def test_decode_far_scores(gpu, B, H, Hkv, n, m, d, dt, alibi, lens):
+    _say("decode far scores B=%d H=%d Hkv=%d n=%d m=%d d=%d %s alibi=%s lens=%s"
+         % (B, H, Hkv, n, m, d, dt, alibi, lens))
+    q, k, v = far_inputs(B, H, Hkv, n, m, d, dt, seed=83)
+    kl = None
+    if lens is not None:
+        kl = np.linspace(lens[0], lens[1], B).astype(np.int32)
+    sl = inputs.alibi_slopes(H) if alibi else None
+    o, lse = run_decode(q, k, v, kl, sl)
+    o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal="bottom_right",
+                                         alibi_slopes=sl, return_lse=True)
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
+    if dt == "bf16":
+        assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]

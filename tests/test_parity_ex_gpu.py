@@ -205,6 +205,79 @@ def test_alibi_causal_steep_slopes(gpu, d, dt, causal, lens):
     assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
 
 
+
+def far_inputs(B, H, Hkv, n, m, d, dt, seed):
+    """Inputs whose every score lies far below 0: q = 48 e0 and key j =
+    (-48 + delta_j) e0 with delta_j in {0, 0.25, 0.5, 0.75}, exact in bf16
+    and fp32, and so are the dot products (-2304 + 48 delta_j).  Scaled to
+    log2 units they lie below -290 (d = 128) or -415 (d = 64), so a weight
+    taken against 0 instead of the row max underflows to exactly 0.  Values
+    come from the shared generator."""
+    _, _, v, _ = inputs.draw(B, Hkv, 1, m, d, d, dt, seed=seed)
+    q = torch.zeros(B, H, n, d)
+    k = torch.zeros(B, Hkv, m, d)
+    q[..., 0] = 48.0
+    k[..., 0] = -48.0 + 0.25 * (torch.arange(m) % 4).float()
+    dtype = torch.bfloat16 if dt == "bf16" else torch.float32
+    return q.to(dtype), k.to(dtype), v
+
+
+# Causal ALiBi walks its keys backwards, so a row whose first walked blocks
+# lie past its diagonal meets its first valid key with no running max yet;
+# that block must take the exact path even though its weights against 0
+# all underflow (a sum of 0).  Without ALiBi (the forward walk) the first
+# block holds key 0.  fp32 adds the bias to raw scores near -2300, a rounding
+# of up to 2300 * 2^-24 that moves each weight by about 1e-5 relative: its
+# values are scaled by 1/4 (exact) so that O stays inside the 1e-5 bar, and
+# its log-sum-exp near -200, carrying the same rounding, is not compared.
+@pytest.mark.parametrize("B,H,Hkv,n,m,d,dt,causal,alibi,lens,variant", [
+    (2, 4, 4, 300, 300, 64, "bf16", "top_left", True, None, "<__bf16, 64, 4, 1, true, true>"),
+    (1, 4, 2, 1100, 1100, 64, "bf16", "top_left", True, None, "<__bf16, 64, 8, 2, true, true>"),
+    (2, 4, 4, 200, 640, 64, "bf16", "bottom_right", True, (300, 640),
+     "<__bf16, 64, 4, 1, true, true>"),
+    (2, 4, 4, 300, 300, 128, "bf16", "top_left", True, (150, 300),
+     "<__bf16, 128, 4, 1, true, true>"),
+    (1, 4, 4, 320, 1280, 128, "bf16", "bottom_right", True, None,
+     "<__bf16, 128, 8, 2, true, true>"),
+    (2, 16, 4, 8192, 8192, 128, "bf16", "top_left", True, None,
+     "<__bf16, 128, 8, 1, true, true>"),
+    (1, 2, 2, 200, 200, 64, "f32", "top_left", True, None, "<float, 64, 4, 1, true, true>"),
+    (1, 2, 2, 200, 200, 128, "f32", "bottom_right", True, (120, 200),
+     "<float, 128, 4, 1, true, true>"),
+    # the forward walk, with and without a causal mask
+    (2, 4, 4, 300, 300, 64, "bf16", "top_left", False, (100, 300),
+     "<__bf16, 64, 4, 1, true, false>"),
+    (2, 4, 2, 150, 400, 128, "bf16", False, True, (1, 400), "<__bf16, 128, 4, 1, false, true>"),
+])
+def test_far_scores_first_valid_key(gpu, B, H, Hkv, n, m, d, dt, causal, alibi, lens, variant):
+    _say("far scores B=%d H=%d Hkv=%d n=%d m=%d d=%d %s %s alibi=%s lens=%s"
+         % (B, H, Hkv, n, m, d, dt, causal, alibi, lens))
+    assert _variant(B, H, Hkv, n, m, d, dt, causal, alibi).endswith(variant)
+    q, k, v = far_inputs(B, H, Hkv, n, m, d, dt, seed=81)
+    if dt == "f32":
+        v = v * 0.25
+    kl = None
+    if lens is not None:
+        kl = np.linspace(lens[0], lens[1], B).astype(np.int32)
+    sl = slopes(H) if alibi else None
+    o, lse = gpu_ex(q, k, v, kl, causal, sl)
+    if B * H * n * m <= 1 << 27:
+        o_ref, lse_ref = oracle.attention_ex(q, k, v, key_lens=kl, causal=causal,
+                                             alibi_slopes=sl, return_lse=True)
+    else:
+        rng = np.random.Generator(np.random.PCG64(82))
+        flat = rng.choice(B * H * n, size=512, replace=False)
+        rows = np.stack([flat // (H * n), (flat // n) % H, flat % n], 1)
+        rows = np.concatenate([rows, [[0, 0, 0], [0, 0, 1], [B - 1, H - 1, n - 1]]]).astype(np.int64)
+        o_ref, lse_ref = oracle.attention_ex_rows(q, k, v, rows, key_lens=kl, causal=causal,
+                                                  alibi_slopes=sl)
+        sel = tuple(torch.from_numpy(rows[:, c]) for c in range(3))
+        o, lse = o[sel], lse[sel]
+    assert maxerr(o, o_ref, "O") <= TOL_O[dt]
+    assert np.array_equal(np.isneginf(oracle.to_f64(lse)), np.isneginf(lse_ref))
+    if dt == "bf16":
+        assert maxerr(lse, lse_ref, "lse") <= TOL_LSE[dt]
+
 WCASES = [
     # B, H, Hkv, n, m, d, dtype, causal, alibi, lens
     (2, 4, 2, 150, 200, 64, "bf16", False, False, (30, 200)),

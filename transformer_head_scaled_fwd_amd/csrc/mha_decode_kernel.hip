@@ -184,7 +184,10 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
     } else {
       P::weights(pf, sc, sl2, (m_run == -__builtin_inff()) ? 0.0f : m_run, lb);
       P::pin(pf);
-      const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && lb > 0.0f);
+      // A row with no running max yet takes the exact path at its first
+      // block with a valid key (keys below row_lim), whatever its weights
+      // against 0 summed to: they may all have underflowed to 0.
+      const bool slow = (lb > 65536.0f) || (m_run == -__builtin_inff() && kb * BC < row_lim);
       if (__any(slow)) exact();
     }
     l_run += lb;
