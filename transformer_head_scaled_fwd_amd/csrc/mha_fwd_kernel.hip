@@ -244,15 +244,21 @@ struct Walk {
       // Weights against the running max as it stands.  Every weight is at
       // most the lane's block sum, so while no lane's sum exceeds 2^16 the
       // running max can stay; otherwise the whole wave takes the exact path:
-      // raise the max, recompute the weights, rescale.  So does a row with
-      // no running max yet that has a valid key in this block (its valid
-      // keys are those below row_lim): its weights were taken against 0 and
-      // may all have underflowed to 0, so their sum cannot tell.
+      // raise the max, recompute the weights, rescale.
+      //
+      // Walked backwards, a row whose first blocks lie past its diagonal
+      // meets its first valid key later, with no running max: its weights
+      // are then taken against 0 and may all have underflowed to 0, so their
+      // sum cannot flag it; its valid keys are those below row_lim, so a
+      // block holding one of them takes the exact path too.  Walked
+      // forwards, the first block holds key 0 and leaves every row with a
+      // valid key with a max.
       float lb = 0.0f;
       weights_at(pf_nxt, s, kb + 1, lb);
       P::pin(pf_nxt);
-      const bool slow = (lb > 65536.0f) ||
-                        (m_run == -__builtin_inff() && block_of(kb + 1) * BC < row_lim);
+      bool slow = lb > 65536.0f;
+      if constexpr (REV)
+        slow = slow || (m_run == -__builtin_inff() && block_of(kb + 1) * BC < row_lim);
       if (__any(slow)) {
         bool grew;
         const float alpha = raise_max(pair_max(block_max(s, kb + 1)), grew);
