@@ -311,9 +311,10 @@ def visible_keys(n, L, causal):
     return np.clip(i + L - n + 1, 0, L)
 
 
-def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=0.0):
     """One extended workload through mha_forward_ex (plus the weights pass
-    when it asks for them), timed like the core workloads."""
+    when it asks for them), timed like the core workloads: a time-based
+    pre-warm, `warmup` untimed launches, then event pairs per launch."""
     from transformer_head_scaled_fwd_amd import inputs
     w = inputs.EXT_WORKLOADS[name]
     dev = "cuda:0"
@@ -370,6 +371,7 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
                                            stream.cuda_stream)
             assert st == 0, st
 
+    pw = prewarm(torch, launch, stream, prewarm_ms) if prewarm_ms > 0 else (0.0, 0)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -398,7 +400,7 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     return {
         "workload": name, "entry": "mha_decode" if w.decode else (
             "mha_forward_ex" + (" + mha_attention_weights" if w.weights else "")),
-        "workspace_bytes": ws_bytes,
+        "workspace_bytes": ws_bytes, "prewarm_ms": pw[0], "prewarm_launches": pw[1],
         "dtype": w.dtype, "B": w.B, "H": w.H, "H_kv": w.H_kv, "n": w.n, "m": w.m, "d": w.d,
         "causal": w.causal, "alibi": w.alibi, "key_lens": None if w.lens is None else list(w.lens),
         "input_sets": len(sets), "launches": steps,
@@ -412,10 +414,10 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     }
 
 
-def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
+def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=0.0):
     """One multi-head layer workload through mha_multihead_forward: the
     Q/K/V projections, the core and the output projection, timed together
-    with HIP events on the launch stream."""
+    with HIP events on the launch stream after a time-based pre-warm."""
     from transformer_head_scaled_fwd_amd import inputs
     w = inputs.LAYER_WORKLOADS[name]
     dev = "cuda:0"
@@ -446,6 +448,7 @@ def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
             ws.data_ptr(), need, w.B, w.n, w.n, w.d_model, w.H, code, stream.cuda_stream)
         assert st == 0, st
 
+    pw = prewarm(torch, launch, stream, prewarm_ms) if prewarm_ms > 0 else (0.0, 0)
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -468,6 +471,7 @@ def bench_layer(torch, mha, name, steps, warmup, rotate_bytes=1 << 30):
     return {
         "workload": name, "entry": "mha_multihead_forward", "dtype": w.dtype, "B": w.B,
         "n": w.n, "d_model": w.d_model, "H": w.H, "causal": w.causal,
+        "prewarm_ms": pw[0], "prewarm_launches": pw[1],
         "key_lens": None if w.lens is None else list(w.lens), "input_sets": len(xs),
         "launches": steps, "layer_ms_mean": kern, "layer_ms_median": statistics.median(per),
         "layer_ms_min": min(per),
@@ -603,6 +607,8 @@ def main():
                          "before it samples rows instead")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="GPU time of untimed headline launches before the warmup steps")
+    ap.add_argument("--prewarm-others-ms", type=float, default=200.0,
+                    help="time-based pre-warm before each other workload's timed launches")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES")
     args = ap.parse_args()
 
@@ -625,9 +631,11 @@ def main():
         # One extended or multi-head-layer workload alone (for profiling):
         # its record, timed like the extended list of the full run.
         if args.workload in inputs.EXT_WORKLOADS:
-            rec = bench_ext(torch, mha, args.workload, args.steps, args.warmup)
+            rec = bench_ext(torch, mha, args.workload, args.steps, args.warmup,
+                            prewarm_ms=args.prewarm_others_ms)
         elif args.workload in inputs.LAYER_WORKLOADS:
-            rec = bench_layer(torch, mha, args.workload, args.steps, args.warmup)
+            rec = bench_layer(torch, mha, args.workload, args.steps, args.warmup,
+                              prewarm_ms=args.prewarm_others_ms)
         else:
             ap.error("unknown workload %r" % args.workload)
         print(json.dumps(rec), flush=True)
@@ -644,7 +652,8 @@ def main():
             if name == w.name:
                 continue
             print("bench: %s" % name, file=sys.stderr, flush=True)
-            res, o_host, sets, o_out = bench_workload(torch, mha, name, 200, 20)
+            res, o_host, sets, o_out = bench_workload(torch, mha, name, 200, 20,
+                                                      prewarm_ms=args.prewarm_others_ms)
             del sets
             others.append(res)
             checks.append((inputs.WORKLOADS[name], o_host, o_out, res))
@@ -653,11 +662,11 @@ def main():
     if not args.no_others:
         for name in inputs.EXT_ORDER:
             print("bench: %s" % name, file=sys.stderr, flush=True)
-            ext.append(bench_ext(torch, mha, name, 100, 20))
+            ext.append(bench_ext(torch, mha, name, 100, 20, prewarm_ms=args.prewarm_others_ms))
             torch.cuda.empty_cache()
         for name in inputs.LAYER_ORDER:
             print("bench: %s" % name, file=sys.stderr, flush=True)
-            ext.append(bench_layer(torch, mha, name, 100, 20))
+            ext.append(bench_layer(torch, mha, name, 100, 20, prewarm_ms=args.prewarm_others_ms))
             torch.cuda.empty_cache()
     traffic = recorded_traffic() if w.name == HEADLINE else None
     cpu = None
