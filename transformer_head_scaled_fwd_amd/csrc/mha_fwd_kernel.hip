@@ -274,10 +274,17 @@ struct Walk {
   }
 };
 
+// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (n + __umulhi(n, f.mul)) >> f.shift;
+}
+
 // Arguments of the forward kernel beyond the tensors.
 struct FwdParams {
   int H;              // query heads
+  int H_kv;           // K/V heads
   int group;          // query heads per K/V head (H / H_kv)
+  int BH;             // batch x query heads
   int n, m;           // query rows, key rows per head
   int nqb;            // query blocks per head
   int bottom_right;   // causal alignment: 0 top-left, 1 bottom-right
@@ -286,6 +293,10 @@ struct FwdParams {
   float scale;        // the caller's scale
   float scale_log2;   // scale * log2(e)
   int stream_out;     // results written through to memory (kStoreOut)
+  // Divisors of the block-index decode, fixed at launch: BH, H and group
+  // (plain order); group * nqb * unit_group, group * unit_group and H_kv
+  // (pinned order).
+  FastDiv div_bh, div_h, div_group, div_gw, div_pg, div_hkv;
 };
 
 // Resident workgroups per CU: one for 8 waves, or when the fp32 d = 128
@@ -328,8 +339,12 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int lane = w.lane, li = w.li, hi = w.hi;
 
   const int n = prm.n, m = prm.m, nqb = prm.nqb;
-  const int bid = blockIdx.x;
-  int qbr, bh;  // query-block rank (0 = first launched) and batch*head
+  const uint32_t bid = blockIdx.x;
+  // Query-block rank (0 = first launched), batch, query head and K/V head of
+  // the workgroup.  The divisions are by launch constants (fdiv), so the
+  // loads below wait on a few scalar instructions instead of division
+  // sequences.
+  int qbr, b, t, bkv;
   if (prm.units_per_xcd > 0) {
     // Workgroups go to the 8 XCDs round-robin in index order, and each XCD
     // has its own L2.  Pin every K/V head (a "unit": its group of query heads
@@ -337,25 +352,28 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     // work through its units unit_group at a time, query-block rank first
     // within the group, so that the workgroups running together on an XCD
     // read the same K/V rows.
-    const int x = bid % 8, r = bid / 8;
-    const int per_group = prm.unit_group * prm.group;  // query heads per unit group
-    const int gw = per_group * nqb;                    // workgroups per unit group
-    const int k = r / gw, w_in = r % gw;
-    qbr = w_in / per_group;
-    const int rest = w_in % per_group;
-    const int u = x + 8 * (k * prm.unit_group + rest / prm.group);
-    const int Hkv = prm.H / prm.group;
-    bh = (u / Hkv) * prm.H + (u % Hkv) * prm.group + rest % prm.group;
+    const uint32_t x = bid % 8, r = bid / 8;
+    const uint32_t k = fdiv(r, prm.div_gw);       // unit group
+    const uint32_t w_in = r - k * prm.div_gw.d;   // workgroup within it
+    qbr = (int)fdiv(w_in, prm.div_pg);
+    const uint32_t rest = w_in - (uint32_t)qbr * prm.div_pg.d;  // query head within the group
+    const uint32_t uq = fdiv(rest, prm.div_group);
+    const uint32_t u = x + 8 * (k * prm.unit_group + uq);       // K/V head: batch * H_kv + g
+    const uint32_t bb = fdiv(u, prm.div_hkv);
+    b = (int)bb;
+    t = (int)((u - bb * prm.H_kv) * prm.group + (rest - uq * prm.group));
+    bkv = (int)u;
   } else {
-    const int BH = gridDim.x / nqb;
-    qbr = bid / BH;
-    bh = bid % BH;
+    qbr = (int)fdiv(bid, prm.div_bh);
+    const uint32_t bh = bid - (uint32_t)qbr * prm.BH;
+    b = (int)fdiv(bh, prm.div_h);
+    t = (int)(bh - (uint32_t)b * prm.H);
+    bkv = b * prm.H_kv + (int)fdiv(t, prm.div_group);
   }
+  const int bh = b * prm.H + t;
   // Heaviest query blocks first for causal attention: the work of a block
   // grows with its index, so launching them in reverse evens out the tail.
   const int qb = CAUSAL ? (nqb - 1 - qbr) : qbr;
-  const int b = bh / prm.H, t = bh % prm.H;
-  const int bkv = b * (prm.H / prm.group) + t / prm.group;  // K/V head
   const int q0 = qb * BR;
   const int row_w = q0 + rg * kRowsPerWave;
   const int my_row = row_w + li;
@@ -611,7 +629,9 @@ static hipError_t launch_one(const LaunchArgs& a) {
   constexpr int BR = Geo<T, D, NW, KS>::BR;
   FwdParams prm;
   prm.H = (int)a.H;
+  prm.H_kv = (int)a.H_kv;
   prm.group = (int)(a.H / a.H_kv);
+  prm.BH = (int)(a.B * a.H);
   prm.n = (int)a.n;
   prm.m = (int)a.m;
   prm.nqb = (int)((a.n + BR - 1) / BR);
@@ -643,6 +663,12 @@ static hipError_t launch_one(const LaunchArgs& a) {
   }
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
+  prm.div_bh = fast_div((uint32_t)prm.BH);
+  prm.div_h = fast_div((uint32_t)prm.H);
+  prm.div_group = fast_div((uint32_t)prm.group);
+  prm.div_gw = fast_div((uint32_t)(prm.unit_group * prm.group * prm.nqb));
+  prm.div_pg = fast_div((uint32_t)(prm.unit_group * prm.group));
+  prm.div_hkv = fast_div((uint32_t)prm.H_kv);
   const int64_t blocks = (int64_t)prm.nqb * a.B * a.H;
   // Results written through to memory when they fit the L2s (kStoreOut).
   prm.stream_out = a.B * a.H * a.n * a.d * (int64_t)sizeof(T) <= kStreamOutMaxBytes;

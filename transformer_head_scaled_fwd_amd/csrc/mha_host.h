@@ -63,6 +63,19 @@ mha_status check_multihead(const void* Xq, const void* Xk, const void* Xv, const
                     const void* workspace, int64_t workspace_bytes, int64_t B, int64_t n,
                     int64_t m, int64_t d_model, int64_t H, mha_dtype dtype);
 
+// Division by a divisor d in [1, 2^31) fixed at launch, for indices n in
+// [0, 2^31): n / d = (n + mulhi(n, mul)) >> shift, where shift = ceil(log2 d)
+// and 2^32 + mul = ceil(2^(32 + shift) / d) (the round-up multiplier of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994).  With 2^shift >= d the multiplier exceeds
+// 2^(32 + shift) / d by less than 1 / d of a unit, and n d < 2^(32 + shift),
+// so the product never carries n / d past the next integer.  Kernels decode
+// their block index with it instead of a run-time division.
+struct FastDiv {
+  uint32_t d, mul, shift;
+};
+FastDiv fast_div(uint32_t d);
+
 // Workgroup shape of the forward kernel for a problem: NW waves per
 // workgroup, KS key groups (see the kernel).  mode: 0 no causal mask, 1
 // causal top-left, 2 causal bottom-right.
