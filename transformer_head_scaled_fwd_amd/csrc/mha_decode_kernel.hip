@@ -46,7 +46,16 @@ struct DecParams {
   int nsplit;            // workgroups along the key axis
   int split_blocks;      // key blocks per split (a multiple of the wave count)
   float scale, scale_log2;
+  int H_kv;              // K/V heads
+  // Divisors of the block-index decode and of a lane's row, fixed at
+  // launch (FastDiv): nsplit, nrs, H_kv and n.
+  FastDiv div_split, div_nrs, div_hkv, div_n;
 };
+
+// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
+__device__ __forceinline__ uint32_t ddiv(uint32_t n, FastDiv f) {
+  return (n + __umulhi(n, f.mul)) >> f.shift;
+}
 
 template <typename T, int D, int NW>
 struct DecGeo {
@@ -76,14 +85,16 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   const int lane = tid % 64, li = lane % 32, hi = lane / 32;
   const int n = prm.n, m = prm.m;
 
-  // grid: ((b * Hkv + g) * nrs + rs) * nsplit + s
-  int bid = blockIdx.x;
-  const int s = bid % prm.nsplit;
-  bid /= prm.nsplit;
-  const int rs = bid % prm.nrs;
-  bid /= prm.nrs;
-  const int Hkv = prm.H / prm.group;
-  const int g = bid % Hkv, b = bid / Hkv;
+  // grid: ((b * Hkv + g) * nrs + rs) * nsplit + s; the divisions are by
+  // launch constants (ddiv)
+  const uint32_t bid0 = blockIdx.x;
+  const uint32_t bid1 = ddiv(bid0, prm.div_split);
+  const int s = (int)(bid0 - bid1 * (uint32_t)prm.nsplit);
+  const uint32_t bid2 = ddiv(bid1, prm.div_nrs);
+  const int rs = (int)(bid1 - bid2 * (uint32_t)prm.nrs);
+  const int Hkv = prm.H_kv;
+  const int b = (int)ddiv(bid2, prm.div_hkv);
+  const int g = (int)bid2 - b * Hkv;
 
   int L = m;
   if (cache_lens != nullptr) {
@@ -95,8 +106,9 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   // token i = r % n.  Lanes past R compute a dummy row that is never stored.
   const int r = rs * kRowsPerWave + li;
   const bool real = r < prm.R;
-  const int t = g * prm.group + (real ? r / n : 0);
-  const int i = real ? r % n : 0;
+  const int rt = (int)ddiv((uint32_t)r, prm.div_n);  // r / n
+  const int t = g * prm.group + (real ? rt : 0);
+  const int i = real ? r - rt * n : 0;
   const int qrow = real ? t * n + i : prm.H * n;  // row within batch b; dummy reads 0
   const int prow = i + L - n;                     // position of the query
   const int row_lim = real ? min(L, prow + 1) : L;
@@ -409,6 +421,11 @@ static hipError_t launch_dec(const DecodeArgs& a, const DecodePlan& p) {
   prm.split_blocks = (int)p.split_blocks;
   prm.scale = a.scale;
   prm.scale_log2 = a.scale_log2;
+  prm.H_kv = (int)a.H_kv;
+  prm.div_split = fast_div((uint32_t)prm.nsplit);
+  prm.div_nrs = fast_div((uint32_t)prm.nrs);
+  prm.div_hkv = fast_div((uint32_t)prm.H_kv);
+  prm.div_n = fast_div((uint32_t)prm.n);
   float* part_o = nullptr;
   float* part_ml = nullptr;
   if (p.nsplit > 1) {

@@ -39,7 +39,15 @@ struct WeightParams {
   float scale;           // the caller's scale
   float scale_log2;      // scale * log2(e)
   int stream_out;        // A written through to memory (kStoreOut)
+  int BH, H_kv;          // batch x query heads, K/V heads
+  // Divisors of the block-index decode, fixed at launch (FastDiv).
+  FastDiv div_bh, div_nqb, div_h, div_group;
 };
+
+// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
+__device__ __forceinline__ uint32_t wdiv(uint32_t n, FastDiv f) {
+  return (n + __umulhi(n, f.mul)) >> f.shift;
+}
 
 // Resident workgroups per CU: two, except fp32 with d = 128, whose K ring and
 // staging take 98 KiB of LDS.
@@ -72,15 +80,19 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, li = lane % 32, hi = lane / 32;
   const int n = prm.n, m = prm.m;
-  // Workgroup index: (chunk, query block, batch * head), the last fastest.
-  const int nkc = (prm.nkb_all + prm.kchunk - 1) / prm.kchunk;
-  const int BH = gridDim.x / (prm.nqb * nkc);
-  const int bh = blockIdx.x % BH, qb = (blockIdx.x / BH) % prm.nqb;
-  const int kc = blockIdx.x / (BH * prm.nqb);
+  // Workgroup index: (chunk, query block, batch * head), the last fastest;
+  // the divisions are by launch constants (wdiv).
+  const uint32_t bid = blockIdx.x;
+  const uint32_t r1 = wdiv(bid, prm.div_bh);             // chunk * nqb + query block
+  const int bh = (int)(bid - r1 * (uint32_t)prm.BH);
+  const uint32_t kcu = wdiv(r1, prm.div_nqb);
+  const int qb = (int)(r1 - kcu * (uint32_t)prm.nqb);
+  const int kc = (int)kcu;
   const int kb0 = kc * prm.kchunk;                      // this chunk's key blocks
   const int kb1 = min(prm.nkb_all, kb0 + prm.kchunk);   // [kb0, kb1)
-  const int b = bh / prm.H, t = bh % prm.H;
-  const int bkv = b * (prm.H / prm.group) + t / prm.group;
+  const int b = (int)wdiv((uint32_t)bh, prm.div_h);
+  const int t = bh - b * prm.H;
+  const int bkv = b * prm.H_kv + (int)wdiv((uint32_t)t, prm.div_group);
   const int q0 = qb * BR;
 
   int L = m;
@@ -293,6 +305,12 @@ static hipError_t launch_w(const WeightsArgs& a) {
   prm.scale_log2 = a.scale_log2;
   // A written through to memory when it fits the L2s (kStoreOut).
   prm.stream_out = a.B * a.H * a.n * a.m * (int64_t)sizeof(T) <= kStreamOutMaxBytes;
+  prm.BH = (int)(a.B * a.H);
+  prm.H_kv = (int)a.H_kv;
+  prm.div_bh = fast_div((uint32_t)prm.BH);
+  prm.div_nqb = fast_div((uint32_t)prm.nqb);
+  prm.div_h = fast_div((uint32_t)prm.H);
+  prm.div_group = fast_div((uint32_t)prm.group);
   const int64_t blocks = units * nkc;
   hipLaunchKernelGGL((attn_weights_kernel<T, D, CAUSAL, ALIBI>), dim3((unsigned)blocks), dim3(256),
                      0, (hipStream_t)a.stream, (const T*)a.Q, (const T*)a.K, a.key_lens,
