@@ -86,6 +86,13 @@ CASES = [
     (2, 4, 2, 300, 900, 128, "bf16", "bottom_right", True, (200, 900)),
     (1, 4, 4, 1200, 1200, 128, "bf16", "top_left", True, None),
     (1, 4, 2, 300, 300, 128, "f32", "top_left", True, (1, 300)),
+    # block-index decode by launch-time divisors that are not powers of two:
+    # K/V heads pinned to XCDs (batch x H_kv a multiple of 8) with groups of 3
+    # and 5 K/V heads per batch, and the plain order with B x H = 15
+    (8, 12, 4, 256, 256, 64, "bf16", "top_left", False, None),
+    (8, 15, 5, 200, 300, 128, "bf16", False, True, (1, 300)),
+    (8, 6, 2, 130, 400, 64, "bf16", "bottom_right", True, (130, 400)),
+    (3, 5, 5, 300, 300, 64, "bf16", "top_left", False, (1, 300)),
 ]
 
 
