@@ -215,6 +215,44 @@ def time_graph(torch, mha, sets, w, launches=64, replays=5):
     return best
 
 
+def time_graph_ext(torch, launch, outs, launches=32, replays=5):
+    """GPU-side time per step of a decode workload (its decode and merge
+    launches), captured `launches` steps at a time in one HIP graph over the
+    rotating input sets, as a serving loop replays its decode steps.  Every
+    replay's outputs are checked bit for bit against eager steps, with eager
+    work and a synchronisation between replays.  Returns microseconds per
+    step (best replay)."""
+    nset = len(outs)
+    for i in range(nset):
+        launch(i)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        for i in range(launches):
+            launch(i)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(replays):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        for j in range(min(nset, launches)):
+            if not torch.equal(outs[j], ref[j]):
+                raise RuntimeError("graph replay differs from the eager steps")
+        us = e0.elapsed_time(e1) * 1e3 / launches
+        best = us if best is None else min(best, us)
+    del g
+    return best
+
+
 def time_copy_floor(torch, nbytes, launches=64, replays=5, rotate_bytes=1 << 30):
     """GPU-side time per launch of a plain device copy that reads nbytes/2 and
     writes nbytes/2 (the same HBM bytes as one attention launch), timed like
@@ -344,13 +382,14 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=
         j = i % len(sets)
         a, b, c = sets[j]
         lib = mha.load()
+        cur = torch.cuda.current_stream().cuda_stream  # the capturing stream under a graph
         mode = mha.mask_mode(w.causal)
         if w.decode:
             st = lib.mha_decode(a.data_ptr(), b.data_ptr(), c.data_ptr(),
                                 None if kld is None else kld.data_ptr(),
                                 None if sld is None else sld.data_ptr(), w.scale,
                                 outs[j].data_ptr(), None, ws.data_ptr(), ws_bytes,
-                                w.B, w.H, w.H_kv, w.n, w.m, w.d, w.d, code, stream.cuda_stream)
+                                w.B, w.H, w.H_kv, w.n, w.m, w.d, w.d, code, cur)
             assert st == 0, st
             return
         st = lib.mha_forward_ex(a.data_ptr(), b.data_ptr(), c.data_ptr(),
@@ -359,7 +398,7 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=
                                 outs[j].data_ptr(), lses[j].data_ptr() if w.weights else None,
                                 w.B, w.H, w.H_kv, w.n, w.m, w.d, w.d,
                                 mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32,
-                                stream.cuda_stream)
+                                cur)
         assert st == 0, st
         if w.weights:
             st = lib.mha_attention_weights(a.data_ptr(), b.data_ptr(),
@@ -368,7 +407,7 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=
                                            lses[j].data_ptr(), wts[j].data_ptr(), w.B, w.H,
                                            w.H_kv, w.n, w.m, w.d,
                                            mha.MHA_BF16 if w.dtype == "bf16" else mha.MHA_F32,
-                                           stream.cuda_stream)
+                                           cur)
             assert st == 0, st
 
     pw = prewarm(torch, launch, stream, prewarm_ms) if prewarm_ms > 0 else (0.0, 0)
@@ -384,6 +423,7 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     kern = statistics.mean(per)
+    graph_us = time_graph_ext(torch, launch, outs) if w.decode else None
     pairs = 0
     kv_rows = 0
     for b in range(w.B):
@@ -410,6 +450,10 @@ def bench_ext(torch, mha, name, steps, warmup, rotate_bytes=1 << 30, prewarm_ms=
         "frac_mfma_peak": useful / (kern * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "gbps": abytes / (kern * 1e-3) / 1e9,
         "frac_hbm": abytes / (kern * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "graph_us_per_step": graph_us,
+        "graph_gbps": None if graph_us is None else abytes / (graph_us * 1e-6) / 1e9,
+        "graph_frac_hbm": None if graph_us is None else
+        abytes / (graph_us * 1e-6) / 1e9 / PEAK_HBM_GBS,
         "algorithmic_bytes": abytes, "useful_flops": useful,
     }
 
