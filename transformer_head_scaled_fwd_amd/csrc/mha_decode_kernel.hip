@@ -52,11 +52,6 @@ struct DecParams {
   FastDiv div_split, div_nrs, div_hkv, div_n;
 };
 
-// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
-__device__ __forceinline__ uint32_t ddiv(uint32_t n, FastDiv f) {
-  return (n + __umulhi(n, f.mul)) >> f.shift;
-}
-
 template <typename T, int D, int NW>
 struct DecGeo {
   using G1 = Geo<T, D, 1>;  // one wave stages a whole tile
@@ -86,14 +81,14 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   const int n = prm.n, m = prm.m;
 
   // grid: ((b * Hkv + g) * nrs + rs) * nsplit + s; the divisions are by
-  // launch constants (ddiv)
+  // launch constants (div_by)
   const uint32_t bid0 = blockIdx.x;
-  const uint32_t bid1 = ddiv(bid0, prm.div_split);
+  const uint32_t bid1 = div_by(bid0, prm.div_split);
   const int s = (int)(bid0 - bid1 * (uint32_t)prm.nsplit);
-  const uint32_t bid2 = ddiv(bid1, prm.div_nrs);
+  const uint32_t bid2 = div_by(bid1, prm.div_nrs);
   const int rs = (int)(bid1 - bid2 * (uint32_t)prm.nrs);
   const int Hkv = prm.H_kv;
-  const int b = (int)ddiv(bid2, prm.div_hkv);
+  const int b = (int)div_by(bid2, prm.div_hkv);
   const int g = (int)bid2 - b * Hkv;
 
   int L = m;
@@ -106,7 +101,7 @@ attn_decode_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp, const T* 
   // token i = r % n.  Lanes past R compute a dummy row that is never stored.
   const int r = rs * kRowsPerWave + li;
   const bool real = r < prm.R;
-  const int rt = (int)ddiv((uint32_t)r, prm.div_n);  // r / n
+  const int rt = (int)div_by((uint32_t)r, prm.div_n);  // r / n
   const int t = g * prm.group + (real ? rt : 0);
   const int i = real ? r - rt * n : 0;
   const int qrow = real ? t * n + i : prm.H * n;  // row within batch b; dummy reads 0

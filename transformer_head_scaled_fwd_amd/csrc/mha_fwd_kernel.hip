@@ -274,11 +274,6 @@ struct Walk {
   }
 };
 
-// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
-__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
-  return (n + __umulhi(n, f.mul)) >> f.shift;
-}
-
 // Arguments of the forward kernel beyond the tensors.
 struct FwdParams {
   int H;              // query heads
@@ -341,7 +336,7 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int n = prm.n, m = prm.m, nqb = prm.nqb;
   const uint32_t bid = blockIdx.x;
   // Query-block rank (0 = first launched), batch, query head and K/V head of
-  // the workgroup.  The divisions are by launch constants (fdiv), so the
+  // the workgroup.  The divisions are by launch constants (div_by), so the
   // loads below wait on a few scalar instructions instead of division
   // sequences.
   int qbr, b, t, bkv;
@@ -353,22 +348,22 @@ attn_fwd_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
     // within the group, so that the workgroups running together on an XCD
     // read the same K/V rows.
     const uint32_t x = bid % 8, r = bid / 8;
-    const uint32_t k = fdiv(r, prm.div_gw);       // unit group
+    const uint32_t k = div_by(r, prm.div_gw);       // unit group
     const uint32_t w_in = r - k * prm.div_gw.d;   // workgroup within it
-    qbr = (int)fdiv(w_in, prm.div_pg);
+    qbr = (int)div_by(w_in, prm.div_pg);
     const uint32_t rest = w_in - (uint32_t)qbr * prm.div_pg.d;  // query head within the group
-    const uint32_t uq = fdiv(rest, prm.div_group);
+    const uint32_t uq = div_by(rest, prm.div_group);
     const uint32_t u = x + 8 * (k * prm.unit_group + uq);       // K/V head: batch * H_kv + g
-    const uint32_t bb = fdiv(u, prm.div_hkv);
+    const uint32_t bb = div_by(u, prm.div_hkv);
     b = (int)bb;
     t = (int)((u - bb * prm.H_kv) * prm.group + (rest - uq * prm.group));
     bkv = (int)u;
   } else {
-    qbr = (int)fdiv(bid, prm.div_bh);
+    qbr = (int)div_by(bid, prm.div_bh);
     const uint32_t bh = bid - (uint32_t)qbr * prm.BH;
-    b = (int)fdiv(bh, prm.div_h);
+    b = (int)div_by(bh, prm.div_h);
     t = (int)(bh - (uint32_t)b * prm.H);
-    bkv = b * prm.H_kv + (int)fdiv(t, prm.div_group);
+    bkv = b * prm.H_kv + (int)div_by(t, prm.div_group);
   }
   const int bh = b * prm.H + t;
   // Heaviest query blocks first for causal attention: the work of a block

@@ -8,6 +8,12 @@
 
 namespace mha {
 
+// n / f.d for 0 <= n < 2^31 by a launch's divisor (FastDiv, mha_host.h): a
+// multiply-high, an add and a shift.
+__device__ __forceinline__ uint32_t div_by(uint32_t n, FastDiv f) {
+  return (n + __umulhi(n, f.mul)) >> f.shift;
+}
+
 // Arguments after host validation; sizes fit the kernels' 32-bit offsets.
 struct LaunchArgs {
   const void* Q;

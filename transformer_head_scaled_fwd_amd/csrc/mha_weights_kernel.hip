@@ -44,11 +44,6 @@ struct WeightParams {
   FastDiv div_bh, div_nqb, div_h, div_group;
 };
 
-// n / f.d for 0 <= n < 2^31, by the launch's multiplier (FastDiv).
-__device__ __forceinline__ uint32_t wdiv(uint32_t n, FastDiv f) {
-  return (n + __umulhi(n, f.mul)) >> f.shift;
-}
-
 // Resident workgroups per CU: two, except fp32 with d = 128, whose K ring and
 // staging take 98 KiB of LDS.
 template <typename T, int D>
@@ -81,18 +76,18 @@ attn_weights_kernel(const T* __restrict__ Qp, const T* __restrict__ Kp,
   const int lane = tid % 64, li = lane % 32, hi = lane / 32;
   const int n = prm.n, m = prm.m;
   // Workgroup index: (chunk, query block, batch * head), the last fastest;
-  // the divisions are by launch constants (wdiv).
+  // the divisions are by launch constants (div_by).
   const uint32_t bid = blockIdx.x;
-  const uint32_t r1 = wdiv(bid, prm.div_bh);             // chunk * nqb + query block
+  const uint32_t r1 = div_by(bid, prm.div_bh);             // chunk * nqb + query block
   const int bh = (int)(bid - r1 * (uint32_t)prm.BH);
-  const uint32_t kcu = wdiv(r1, prm.div_nqb);
+  const uint32_t kcu = div_by(r1, prm.div_nqb);
   const int qb = (int)(r1 - kcu * (uint32_t)prm.nqb);
   const int kc = (int)kcu;
   const int kb0 = kc * prm.kchunk;                      // this chunk's key blocks
   const int kb1 = min(prm.nkb_all, kb0 + prm.kchunk);   // [kb0, kb1)
-  const int b = (int)wdiv((uint32_t)bh, prm.div_h);
+  const int b = (int)div_by((uint32_t)bh, prm.div_h);
   const int t = bh - b * prm.H;
-  const int bkv = b * prm.H_kv + (int)wdiv((uint32_t)t, prm.div_group);
+  const int bkv = b * prm.H_kv + (int)div_by((uint32_t)t, prm.div_group);
   const int q0 = qb * BR;
 
   int L = m;
