@@ -243,6 +243,16 @@ mha_status check_multihead(const void* Xq, const void* Xk, const void* Xv, const
   return MHA_OK;
 }
 
+FastDiv fast_div(uint32_t d) {
+  FastDiv f{d, 0, 0};
+  if (d == 0) return f;  // not a divisor; callers pass d >= 1
+  while (f.shift < 31 && (1u << f.shift) < d) ++f.shift;
+  // ceil(2^(32 + shift) / d) - 2^32, below 2^32 for every d >= 1
+  const uint64_t num = (uint64_t)1 << (32 + f.shift);
+  f.mul = (uint32_t)((num + d - 1) / d - ((uint64_t)1 << 32));
+  return f;
+}
+
 // Workgroup shape:
 //  - 8 waves as 8 row groups (256 query rows, one workgroup per CU) for bf16
 //    with d = 128 when the query axis gives every CU several workgroups and
@@ -261,16 +271,6 @@ mha_status check_multihead(const void* Xq, const void* Xk, const void* Xv, const
 //    so shorter walks keep one key group (measured: m = 256 and 512 lose
 //    4-11%, m = 1024, 2048 and 4096 gain 4%, 9% and 12%);
 //  - otherwise 4 waves (128 rows, two workgroups per CU).
-FastDiv fast_div(uint32_t d) {
-  FastDiv f{d, 0, 0};
-  if (d == 0) return f;  // not a divisor; callers pass d >= 1
-  while (f.shift < 31 && (1u << f.shift) < d) ++f.shift;
-  // ceil(2^(32 + shift) / d) - 2^32, below 2^32 for every d >= 1
-  const uint64_t num = (uint64_t)1 << (32 + f.shift);
-  f.mul = (uint32_t)((num + d - 1) / d - ((uint64_t)1 << 32));
-  return f;
-}
-
 FwdVariant forward_variant(bool bf16, int d, int64_t B, int64_t H, int64_t n, int64_t m,
                            int mode) {
   if (bf16) {
